@@ -1,0 +1,124 @@
+// Device helpers shared by the libgdn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// ---------------------------------------------------------------- bf16 --
+// bf16 is handled as raw uint16 bit patterns: widening is a shift, narrowing
+// rounds to nearest with ties to even (inputs are finite).
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Element type tags for the io dtype.
+struct IoBf16 { using T = uint16_t; static constexpr int kBytes = 2; };
+struct IoF32 { using T = float; static constexpr int kBytes = 4; };
+
+// Load 8 consecutive io elements (16-byte aligned for bf16) as fp32.
+template <typename IO>
+__device__ __forceinline__ void load8(const typename IO::T* p, float* out);
+
+template <>
+__device__ __forceinline__ void load8<IoBf16>(const uint16_t* p, float* out) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  const uint32_t r[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(r[i] << 16);
+    out[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8<IoF32>(const float* p, float* out) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+template <typename IO>
+__device__ __forceinline__ float load1(const typename IO::T* p);
+template <>
+__device__ __forceinline__ float load1<IoBf16>(const uint16_t* p) { return bf16_to_f32(*p); }
+template <>
+__device__ __forceinline__ float load1<IoF32>(const float* p) { return *p; }
+
+template <typename IO>
+__device__ __forceinline__ void store1(typename IO::T* p, float x);
+template <>
+__device__ __forceinline__ void store1<IoBf16>(uint16_t* p, float x) { *p = (uint16_t)f32_to_bf16(x); }
+template <>
+__device__ __forceinline__ void store1<IoF32>(float* p, float x) { *p = x; }
+
+// Store 8 fp32 values as 8 consecutive io elements.
+template <typename IO>
+__device__ __forceinline__ void store8(typename IO::T* p, const float* v);
+template <>
+__device__ __forceinline__ void store8<IoBf16>(uint16_t* p, const float* v) {
+  uint4 w;
+  w.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+  w.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  w.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+  w.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+  *reinterpret_cast<uint4*>(p) = w;
+}
+template <>
+__device__ __forceinline__ void store8<IoF32>(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// 16 consecutive fp32 values, 16-byte aligned.
+__device__ __forceinline__ void load16f(const float* p, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 a = reinterpret_cast<const float4*>(p)[i];
+    out[4 * i] = a.x; out[4 * i + 1] = a.y; out[4 * i + 2] = a.z; out[4 * i + 3] = a.w;
+  }
+}
+__device__ __forceinline__ void store16f(float* p, const float* v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
+// ------------------------------------------------------- lane reductions --
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 64);
+// every lane of the group receives the same total, summed in a fixed order.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < W; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// First index i in [0, n) with a[i] >= key (n when none); a ascending.
+__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < key) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Index s of the sequence holding token p: cu[s] <= p < cu[s+1] (n_seqs >= 1,
+// empty sequences skipped).  cu ascending, cu[0] = 0, p < cu[n_seqs].
+__device__ __forceinline__ int seq_of_token(const int32_t* cu, int n_seqs, int p) {
+  int lo = 0, hi = n_seqs;  // invariant: cu[lo] <= p < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace gdn

@@ -1,0 +1,174 @@
+// Token-recurrent gated delta rule on fp32 VALU: the one-token decode step on
+// a state pool, and a token-by-token prefill used for the fp32 io path.
+//
+// Work split: one workgroup owns 32 rows (value dims) of one (sequence, value
+// head) state; each row is spread over DK/16 consecutive lanes holding 16
+// consecutive key dims in registers.  Row sums (S k, S q, |k|^2, |q|^2) are
+// lane-group reductions in a fixed order, so a row's arithmetic never depends
+// on which workgroup or launch computes it.
+#include <climits>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kRows = 32;  // state rows per workgroup
+
+// One token of the recurrence for this lane's 16 state entries.
+//   S <- alpha S + u k^T,  u = beta (v - alpha S k)   (= alpha S (I - beta k k^T) + beta v k^T)
+// Returns o = S q (already summed over the row's lanes).
+template <int LPR>
+__device__ __forceinline__ float token_step(float* S, float* kv, float* qv, float vrow, float g,
+                                            float beta, int l2norm, float eps) {
+  if (l2norm) {
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { sk = fmaf(kv[i], kv[i], sk); sq = fmaf(qv[i], qv[i], sq); }
+    sk = group_sum<LPR>(sk);
+    sq = group_sum<LPR>(sq);
+    const float rk = 1.0f / sqrtf(sk + eps), rq = 1.0f / sqrtf(sq + eps);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { kv[i] *= rk; qv[i] *= rq; }
+  }
+  const float alpha = expf(g);
+  float x = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x = fmaf(S[i], kv[i], x);
+  x = group_sum<LPR>(x);
+  const float u = beta * (vrow - alpha * x);
+  float o = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    S[i] = fmaf(alpha, S[i], u * kv[i]);
+    o = fmaf(S[i], qv[i], o);
+  }
+  return group_sum<LPR>(o);
+}
+
+template <int DK, int DV, typename IO>
+__global__ void __launch_bounds__(kRows * (DK / 16))
+recurrent_prefill_kernel(const ScanArgs a) {
+  constexpr int LPR = DK / 16;
+  using T = typename IO::T;
+  const int s = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.z * kRows + tid / LPR;
+  const int kb = (tid % LPR) * 16;
+  const int j = h / (a.Hv / a.Hqk);
+  const int t0 = a.cu[s], t1 = a.cu[s + 1];
+
+  float S[16];
+  const size_t head_off = ((size_t)h * DV + row) * DK + kb;
+  const size_t state_stride = (size_t)a.Hv * DV * DK;
+  if (a.init) load16f(a.init + (size_t)s * state_stride + head_off, S);
+  else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[i] = 0.f;
+  }
+  int ci = lower_bound_i32(a.ckpt, a.n_ckpt, t0 + 1);
+  int next = ci < a.n_ckpt ? a.ckpt[ci] : INT_MAX;
+
+  const T* qp = static_cast<const T*>(a.q);
+  const T* kp = static_cast<const T*>(a.k);
+  const T* vp = static_cast<const T*>(a.v);
+  T* op = static_cast<T*>(a.out);
+  for (int t = t0; t < t1; ++t) {
+    float kv[16], qv[16];
+    load8<IO>(kp + (size_t)t * a.k_stride + j * DK + kb, kv);
+    load8<IO>(kp + (size_t)t * a.k_stride + j * DK + kb + 8, kv + 8);
+    load8<IO>(qp + (size_t)t * a.q_stride + j * DK + kb, qv);
+    load8<IO>(qp + (size_t)t * a.q_stride + j * DK + kb + 8, qv + 8);
+    const float vrow = load1<IO>(vp + (size_t)t * a.v_stride + (size_t)h * DV + row);
+    const float g = a.g[(size_t)t * a.Hv + h], beta = a.beta[(size_t)t * a.Hv + h];
+    const float o = token_step<LPR>(S, kv, qv, vrow, g, beta, a.l2norm, a.eps);
+    if (tid % LPR == 0) store1<IO>(op + ((size_t)t * a.Hv + h) * DV + row, a.scale * o);
+    if (t + 1 == next) {
+      store16f(a.ckpt_buf + (size_t)ci * state_stride + head_off, S);
+      ++ci;
+      next = ci < a.n_ckpt ? a.ckpt[ci] : INT_MAX;
+    }
+  }
+  if (a.final_state) store16f(a.final_state + (size_t)s * state_stride + head_off, S);
+}
+
+template <int DK, int DV, typename IO>
+__global__ void __launch_bounds__(kRows * (DK / 16))
+decode_kernel(const DecodeArgs a) {
+  constexpr int LPR = DK / 16;
+  using T = typename IO::T;
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.z * kRows + tid / LPR;
+  const int kb = (tid % LPR) * 16;
+  const int j = h / (a.Hv / a.Hqk);
+  const int r = a.slot ? a.slot[b] : b;
+  float* sp = a.state + (((size_t)r * a.Hv + h) * DV + row) * DK + kb;
+  float S[16], kv[16], qv[16];
+  load16f(sp, S);
+  const T* kp = static_cast<const T*>(a.k) + (size_t)b * a.k_stride + j * DK + kb;
+  const T* qp = static_cast<const T*>(a.q) + (size_t)b * a.q_stride + j * DK + kb;
+  load8<IO>(kp, kv);
+  load8<IO>(kp + 8, kv + 8);
+  load8<IO>(qp, qv);
+  load8<IO>(qp + 8, qv + 8);
+  const float vrow = load1<IO>(static_cast<const T*>(a.v) + (size_t)b * a.v_stride + (size_t)h * DV + row);
+  const float o = token_step<LPR>(S, kv, qv, vrow, a.g[(size_t)b * a.Hv + h],
+                                  a.beta[(size_t)b * a.Hv + h], a.l2norm, a.eps);
+  store16f(sp, S);
+  if (tid % LPR == 0)
+    store1<IO>(static_cast<T*>(a.out) + ((size_t)b * a.Hv + h) * DV + row, a.scale * o);
+}
+
+template <int DK, int DV, typename IO>
+hipError_t launch_rec_prefill(const ScanArgs& a, hipStream_t st) {
+  dim3 grid(a.n_seqs, a.Hv, DV / kRows);
+  hipLaunchKernelGGL((recurrent_prefill_kernel<DK, DV, IO>), grid, dim3(kRows * (DK / 16)), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, typename IO>
+hipError_t launch_dec(const DecodeArgs& a, hipStream_t st) {
+  dim3 grid(a.batch, a.Hv, DV / kRows);
+  hipLaunchKernelGGL((decode_kernel<DK, DV, IO>), grid, dim3(kRows * (DK / 16)), 0, st, a);
+  return hipGetLastError();
+}
+
+#define GDN_DISPATCH(FN, ARGS, ST)                                                     \
+  do {                                                                                 \
+    const int dk_ = (ARGS).dk, dv_ = (ARGS).dv;                                        \
+    const bool b_ = (ARGS).bf16 != 0;                                                  \
+    if (b_) {                                                                          \
+      if (dk_ == 32 && dv_ == 32) return FN<32, 32, IoBf16>(ARGS, ST);                  \
+      if (dk_ == 32 && dv_ == 64) return FN<32, 64, IoBf16>(ARGS, ST);                  \
+      if (dk_ == 32 && dv_ == 128) return FN<32, 128, IoBf16>(ARGS, ST);                \
+      if (dk_ == 64 && dv_ == 32) return FN<64, 32, IoBf16>(ARGS, ST);                  \
+      if (dk_ == 64 && dv_ == 64) return FN<64, 64, IoBf16>(ARGS, ST);                  \
+      if (dk_ == 64 && dv_ == 128) return FN<64, 128, IoBf16>(ARGS, ST);                \
+      if (dk_ == 128 && dv_ == 32) return FN<128, 32, IoBf16>(ARGS, ST);                \
+      if (dk_ == 128 && dv_ == 64) return FN<128, 64, IoBf16>(ARGS, ST);                \
+      if (dk_ == 128 && dv_ == 128) return FN<128, 128, IoBf16>(ARGS, ST);              \
+    } else {                                                                           \
+      if (dk_ == 32 && dv_ == 32) return FN<32, 32, IoF32>(ARGS, ST);                   \
+      if (dk_ == 32 && dv_ == 64) return FN<32, 64, IoF32>(ARGS, ST);                   \
+      if (dk_ == 32 && dv_ == 128) return FN<32, 128, IoF32>(ARGS, ST);                 \
+      if (dk_ == 64 && dv_ == 32) return FN<64, 32, IoF32>(ARGS, ST);                   \
+      if (dk_ == 64 && dv_ == 64) return FN<64, 64, IoF32>(ARGS, ST);                   \
+      if (dk_ == 64 && dv_ == 128) return FN<64, 128, IoF32>(ARGS, ST);                 \
+      if (dk_ == 128 && dv_ == 32) return FN<128, 32, IoF32>(ARGS, ST);                 \
+      if (dk_ == 128 && dv_ == 64) return FN<128, 64, IoF32>(ARGS, ST);                 \
+      if (dk_ == 128 && dv_ == 128) return FN<128, 128, IoF32>(ARGS, ST);               \
+    }                                                                                  \
+    return hipErrorInvalidValue;                                                       \
+  } while (0)
+
+}  // namespace
+
+hipError_t launch_prefill_recurrent(const ScanArgs& a, hipStream_t st) {
+  GDN_DISPATCH(launch_rec_prefill, a, st);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) { GDN_DISPATCH(launch_dec, a, st); }
+
+}  // namespace gdn

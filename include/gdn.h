@@ -1,0 +1,219 @@
+/*
+ * libgdn: packed (varlen) gated-delta-rule prefill with prefix-cache
+ * checkpoints, a one-token decode step, the short convolution ahead of them
+ * and a checkpoint copy on its own stream, for AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes
+ *   Per prompt s and value head h (qk head j = h / (Hv / Hqk)), starting from
+ *   S = init_state[s, h] (zeros when init_state is NULL), for every token t
+ *   of the prompt in order, with alpha_t = exp(g_t):
+ *       S   <- alpha_t * S (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T
+ *       o_t  = scale * S q^_t
+ *   S is head_v_dim x head_k_dim.  k^ and q^ are k and q divided by
+ *   sqrt(sum x^2 + l2_eps) when GDN_QK_L2NORM is set.  This is the gated
+ *   delta rule (Yang, Kautz & Hatamizadeh, "Gated Delta Networks", ICLR 2025).
+ *
+ *   Several prompts share one packed pass and each keeps its own state, so a
+ *   prompt's outputs, checkpoints and final state are bit-identical whether it
+ *   runs alone or packed (sparkinfer release v0.6.28: packed prompt passes;
+ *   "Measured": checkpoints identical alone or packed).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are row-major with the innermost dimension contiguous.  Device
+ *     pointers are HIP device memory (or, where stated, device-mapped pinned
+ *     host memory).  The caller owns every buffer; no call allocates memory.
+ *   - All arguments are validated on the host before anything is enqueued.
+ *     A call that returns an error has enqueued no work (GDN_ERR_HIP: the
+ *     library synchronised the stream it used before returning, so nothing it
+ *     launched is still in flight).
+ *   - Work is asynchronous on the given stream (a hipStream_t passed as
+ *     void*; NULL = the null stream).  The library keeps no global mutable
+ *     state and shares no scratch memory between calls or streams.
+ *   - Launch configuration depends only on the shape struct, never on the
+ *     number of prompts, their lengths or their order.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GDN_API __attribute__((visibility("default")))
+#else
+#define GDN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+  GDN_ERR_SHAPE = 2,       /* negative count, bad stride or inconsistent sizes            */
+  GDN_ERR_UNSUPPORTED = 3, /* head dims, chunk, dtype, flags or head ratio not built      */
+  GDN_ERR_SEQLENS = 4,     /* cu_seqlens not 0-based, non-decreasing, ending at n_tokens  */
+  GDN_ERR_CKPT = 5,        /* checkpoints unsorted, outside a prompt or off its chunk grid */
+  GDN_ERR_CAPACITY = 6,    /* an output list is too short, or a slot outside the pool      */
+  GDN_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed                  */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+/* shape.flags */
+#define GDN_QK_L2NORM 1u
+
+/* Layer geometry and numeric options, passed by pointer to every call.
+ *   num_qk_heads, num_v_heads: Hqk and Hv, Hv a multiple of Hqk.
+ *   head_k_dim, head_v_dim:    dk and dv, each one of 32, 64, 128.
+ *   chunk:                     tokens per chunk of the chunked scan, one of 16,
+ *                              32, 64; checkpoints must sit on this grid.
+ *   io_dtype:                  gdn_dtype of q, k, v, out, x, y, conv states.
+ *   flags:                     GDN_QK_L2NORM or 0.
+ *   scale:                     factor on the outputs (1.0 for none).
+ *   l2_eps:                    added to sum x^2 before the square root.
+ *   q/k/v_tok_stride:          elements between consecutive tokens of q, k, v
+ *                              (0 = dense: Hqk*dk, Hqk*dk, Hv*dv), so q, k and
+ *                              v may be column views of one [T, conv_dim] row. */
+typedef struct gdn_shape {
+  int32_t num_qk_heads;
+  int32_t num_v_heads;
+  int32_t head_k_dim;
+  int32_t head_v_dim;
+  int32_t chunk;
+  int32_t io_dtype;
+  uint32_t flags;
+  float scale;
+  float l2_eps;
+  int32_t reserved;
+  int64_t q_tok_stride;
+  int64_t k_tok_stride;
+  int64_t v_tok_stride;
+} gdn_shape;
+
+/* Human-readable name of a status code (static string, never NULL). */
+GDN_API const char* gdn_status_string(int32_t status);
+
+/* Checkpoint planner (host only, no HIP call).
+ * Source: sparkinfer release v0.6.28, the bullet on checkpoints that fall in
+ * a prompt's last 16 tokens moving back one block so the prompt stays in the
+ * pack.  For prompt s (length L = cu[s+1]-cu[s], absolute first position
+ * p0[s], 0 when p0_host is NULL) every multiple c of `block` with
+ * p0 < c <= p0 + L is taken; if p0 + L - c < tail it moves back to c - block;
+ * it is kept when still > p0 and not already taken.  Writes the global pack
+ * offsets cu[s] + (c - p0), ascending, to out_pos[0 .. *n_out).
+ *   cu_host:   host int32 [n_seqs + 1], validated like gdn_prefill_packed's.
+ *   block:     >= 1.  tail: >= 0 (16 on the page).
+ *   out_pos:   host int32 [cap]; may be NULL when cap == 0 (count only).
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE (n_seqs < 0, block < 1, tail < 0,
+ * p0 < 0), GDN_ERR_SEQLENS, GDN_ERR_CAPACITY (more than cap positions;
+ * *n_out still receives the full count). */
+GDN_API gdn_status gdn_plan_checkpoints(const int32_t* cu_host, int32_t n_seqs, const int32_t* p0_host,
+                                int32_t block, int32_t tail, int32_t* out_pos, int32_t cap,
+                                int32_t* n_out);
+
+/* Width-4 causal depthwise conv + SiLU over a pack, never reading across a
+ * prompt boundary (the short convolution ahead of q, k, v in Gated Delta
+ * Networks' block design).  For channel c and token p of prompt s:
+ *     y[p, c] = silu( sum_{j=0..3} w[c, j] * xs[p - 3 + j, c] )
+ * where xs is the prompt's own inputs and, before its first token, its conv
+ * state (zeros when conv_state_in is NULL).
+ *   conv_dim = 2*Hqk*dk + Hv*dv, channels ordered [q | k | v].
+ *   cu_seqlens / cu_seqlens_host: device / host int32 [n_seqs + 1].
+ *   x, y:            device [n_tokens, conv_dim] io_dtype, token strides in
+ *                    elements (0 = conv_dim); y must not overlap x.
+ *   weight:          device fp32 [conv_dim, 4], tap 3 on the current token.
+ *   conv_state_in:   device io_dtype [n_seqs, 3, conv_dim] oldest first, or NULL.
+ *   conv_state_out:  device io_dtype [n_seqs, 3, conv_dim] or NULL: each
+ *                    prompt's last three inputs (reaching into its history
+ *                    when shorter than 3).  May equal conv_state_in.
+ *   ckpt_positions(_host), n_ckpt: as in gdn_prefill_packed; when conv_ckpt
+ *                    is non-NULL it receives, per checkpoint, the three
+ *                    inputs before it: io_dtype [n_ckpt, 3, conv_dim].
+ * Errors: as gdn_prefill_packed. */
+GDN_API gdn_status gdn_conv1d_silu_packed(const gdn_shape* shape, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int32_t n_seqs,
+                                  int32_t n_tokens, const void* x, int64_t x_tok_stride,
+                                  const float* weight, const void* conv_state_in, void* y,
+                                  int64_t y_tok_stride, void* conv_state_out,
+                                  const int32_t* ckpt_positions,
+                                  const int32_t* ckpt_positions_host, int32_t n_ckpt,
+                                  void* conv_ckpt, void* stream);
+
+/* Packed prefill: the chunked gated-delta-rule scan over every prompt of a
+ * pack, writing outputs, the state at each checkpoint and each prompt's
+ * final state (sparkinfer release v0.6.28: packed passes and prefix-cache
+ * checkpoints of the linear-attention state).
+ *   cu_seqlens:       device int32 [n_seqs + 1]; cu_seqlens_host its host
+ *                     mirror (validated: cu[0] = 0, non-decreasing,
+ *                     cu[n_seqs] = n_tokens).  Empty prompts are allowed
+ *                     (their final state is their initial state).
+ *   q, k:             device io_dtype [n_tokens, Hqk, dk] (token stride from
+ *                     shape); v: [n_tokens, Hv, dv].
+ *   g, beta:          device fp32 [n_tokens, Hv]: log-gate (alpha = exp g)
+ *                     and write strength.
+ *   init_state:       device fp32 [n_seqs, Hv, dv, dk] or NULL (zeros).
+ *   ckpt_positions:   device int32 [n_ckpt] global pack offsets, strictly
+ *                     increasing; ckpt_positions_host its host mirror.  A
+ *                     position p belongs to the prompt with cu[s] < p <=
+ *                     cu[s+1] and must satisfy (p - cu[s]) % chunk == 0; the
+ *                     checkpoint is the state after the prompt's first
+ *                     p - cu[s] tokens.  gdn_plan_checkpoints makes such lists.
+ *   out:              device io_dtype [n_tokens, Hv, dv] (dense).
+ *   final_state:      device fp32 [n_seqs, Hv, dv, dk] or NULL (not written).
+ *   ckpt_buf:         device fp32 [n_ckpt, Hv, dv, dk]; may be NULL iff n_ckpt = 0.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS,
+ * GDN_ERR_CKPT, GDN_ERR_HIP.  init_state may alias final_state. */
+GDN_API gdn_status gdn_prefill_packed(const gdn_shape* shape, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t n_tokens,
+                              const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const float* init_state,
+                              const int32_t* ckpt_positions, const int32_t* ckpt_positions_host,
+                              int32_t n_ckpt, void* out, float* final_state, float* ckpt_buf,
+                              void* stream);
+
+/* One recurrent step for each of `batch` decoding sequences, in place on a
+ * state pool (one forward pass carries decodes beside a packed prefill:
+ * sparkinfer release v0.6.4, "What changed").
+ *   q, k:       device io_dtype [batch, Hqk, dk] (token stride from shape);
+ *   v:          [batch, Hv, dv];  g, beta: device fp32 [batch, Hv].
+ *   state:      device fp32 [pool_slots, Hv, dv, dk], updated in place.
+ *   slot:       device int32 [batch] pool rows, or NULL for rows 0..batch-1;
+ *               slot_host its host mirror (required with slot): every entry
+ *               in [0, pool_slots) and all distinct.
+ *   out:        device io_dtype [batch, Hv, dv].
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_CAPACITY
+ * (slot outside the pool, repeated, or batch > pool_slots without slots),
+ * GDN_ERR_HIP. */
+GDN_API gdn_status gdn_decode_step(const gdn_shape* shape, int32_t batch, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta, float* state,
+                           int64_t pool_slots, const int32_t* slot, const int32_t* slot_host,
+                           void* out, void* stream);
+
+/* Checkpoint copy on its own stream (sparkinfer release v0.6.28: the scan and
+ * the checkpoint copy of checkpointing prompts run on their own streams, and
+ * pinned host buffers for checkpoints are allocated when the prefix cache
+ * starts, never mid-pass).  copy_stream first waits on wait_event (when
+ * non-NULL, typically recorded after gdn_prefill_packed), then a gather
+ * kernel copies item i (bytes_each bytes at ckpt_buf + i * bytes_each) to
+ * dst_pool + dst_slot[i] * bytes_each, then done_event (when non-NULL) is
+ * recorded on copy_stream.
+ *   ckpt_buf:      device memory, n * bytes_each bytes.
+ *   bytes_each:    > 0 and a multiple of 16; both pointers 16-byte aligned.
+ *   dst_pool:      device memory or device-mapped pinned host memory (e.g.
+ *                  from hipHostMalloc), pool_slots * bytes_each bytes.
+ *   dst_slot:      device int64 [n]; dst_slot_host its host mirror, each in
+ *                  [0, pool_slots) and all distinct.
+ *   wait_event, done_event: hipEvent_t as void*, or NULL.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_CAPACITY, GDN_ERR_HIP. */
+GDN_API gdn_status gdn_snapshot_copy(const void* ckpt_buf, int32_t n, int64_t bytes_each, void* dst_pool,
+                             int64_t pool_slots, const int64_t* dst_slot,
+                             const int64_t* dst_slot_host, void* wait_event, void* copy_stream,
+                             void* done_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

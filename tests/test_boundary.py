@@ -1,0 +1,163 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, its planner equals the oracle's, and every validation error
+is returned from the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_prefill_varlen_amd as gdn
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+# Fake device addresses (16-byte aligned) used only in calls that must fail
+# validation; never run where a GPU is present.
+FAKE = 0x100000
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="host-validation probes with fake device pointers run only without a GPU")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"GDN_API\s+[\w\s\*]+?\b(gdn_\w+)\s*\(", text)))
+
+
+def test_header_declares_exactly_the_exported_symbols():
+    assert declared_symbols() == sorted(gdn.EXPORTED)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = gdn.load()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert gdn.gdn_status_string(0) == "GDN_OK"
+    for code in range(1, 8):
+        assert gdn.gdn_status_string(code).startswith(gdn.STATUS[code])
+    assert "unknown" in gdn.gdn_status_string(99)
+
+
+def test_planner_matches_oracle_planner():
+    rng = np.random.default_rng(0)
+    for block in (16, 32, 64, 256, 1024):
+        for trial in range(40):
+            n = int(rng.integers(0, 9))
+            lens = rng.integers(0, 5 * block + 40, size=n)
+            cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            p0 = (rng.integers(0, 4, size=n) * block).astype(np.int32)
+            for pz in (None, p0):
+                got = gdn.gdn_plan_checkpoints(cu, block, 16, pz)
+                want = O.plan_checkpoints(cu, block, 16, p0=pz)
+                np.testing.assert_array_equal(got, want)
+
+
+def test_planner_errors_and_capacity():
+    lib = gdn.load()
+    cu = np.array([0, 1024, 2048], np.int32)
+    n = ctypes.c_int32(-1)
+    out = np.zeros(2, np.int32)
+    st = lib.gdn_plan_checkpoints(cu.ctypes.data, 2, None, 256, 16, out.ctypes.data, 2, ctypes.byref(n))
+    assert st == 6 and n.value == 6 and list(out) == [256, 512]
+    assert lib.gdn_plan_checkpoints(cu.ctypes.data, 2, None, 0, 16, None, 0, ctypes.byref(n)) == 2
+    bad = np.array([0, 10, 5], np.int32)
+    assert lib.gdn_plan_checkpoints(bad.ctypes.data, 2, None, 16, 16, None, 0, ctypes.byref(n)) == 4
+    assert lib.gdn_plan_checkpoints(None, 2, None, 16, 16, None, 0, ctypes.byref(n)) == 1
+
+
+def _prefill_call(shape=None, cu=(0, 40, 64), T=None, ck=(), ptr=FAKE, ckbuf=True, q=None, out=None):
+    lib = gdn.load()
+    shape = shape if shape is not None else gdn.make_shape(2, 2, 32, 32, 16, gdn.GDN_F32)
+    cu = np.asarray(cu, np.int32)
+    T = int(cu[-1]) if T is None else T
+    ck = np.asarray(ck, np.int32)
+    q = ptr if q is None else q
+    return lib.gdn_prefill_packed(ctypes.byref(shape) if shape is not False else None, ptr,
+                                  cu.ctypes.data, len(cu) - 1, T, q, ptr, ptr, ptr, ptr, None,
+                                  ptr if len(ck) else None, ck.ctypes.data if len(ck) else None,
+                                  len(ck), ptr if out is None else out, ptr,
+                                  ptr if (ckbuf and len(ck)) else None, None)
+
+
+@no_gpu
+def test_prefill_validation_errors():
+    S = lambda **kw: gdn.make_shape(**{**dict(Hqk=2, Hv=2, dk=32, dv=32, chunk=16,
+                                              io_dtype=gdn.GDN_F32), **kw})
+    assert _prefill_call(shape=False) == 1
+    assert _prefill_call(S(Hqk=2, Hv=3)) == 3
+    assert _prefill_call(S(dk=48)) == 3
+    assert _prefill_call(S(dv=256)) == 3
+    assert _prefill_call(S(chunk=128)) == 3
+    assert _prefill_call(S(io_dtype=5)) == 3
+    sh = S(); sh.flags = 2
+    assert _prefill_call(sh) == 3
+    sh = S(); sh.l2_eps = -1.0
+    assert _prefill_call(sh) == 2
+    assert _prefill_call(S(Hqk=0)) == 2
+    assert _prefill_call(cu=(1, 40, 64)) == 4
+    assert _prefill_call(cu=(0, 40, 30)) == 4
+    assert _prefill_call(cu=(0, 40, 64), T=65) == 4
+    assert _prefill_call(q=0) == 1
+    assert _prefill_call(ck=(32, 16)) == 5          # not increasing
+    assert _prefill_call(ck=(8,)) == 5              # off the 16-token chunk grid
+    assert _prefill_call(ck=(0,)) == 5              # not inside a prompt
+    assert _prefill_call(ck=(80,)) == 5             # past the pack
+    assert _prefill_call(ck=(16,), ckbuf=False) == 1
+    assert _prefill_call(out=FAKE + 4) == 2         # misaligned
+    assert _prefill_call(S(q_tok_stride=32)) == 2   # shorter than one token row
+    assert _prefill_call(S(k_tok_stride=65)) == 2   # rows not 16-byte aligned
+
+
+def test_empty_pack_is_ok_without_any_launch():
+    assert _prefill_call(cu=(0,)) == 0
+
+
+@no_gpu
+def test_decode_validation_errors():
+    lib = gdn.load()
+    sh = gdn.make_shape(2, 4, 32, 32, 16)
+    def call(batch=3, pool=5, slot=None):
+        sl = None if slot is None else np.asarray(slot, np.int32)
+        return lib.gdn_decode_step(ctypes.byref(sh), batch, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, pool,
+                                   FAKE if sl is not None else None,
+                                   sl.ctypes.data if sl is not None else None, FAKE, None)
+    assert call(batch=0) == 0
+    assert call(batch=6, pool=5) == 6
+    assert call(slot=[0, 1, 1]) == 6
+    assert call(slot=[0, 1, 5]) == 6
+    assert call(slot=[0, -1, 2]) == 6
+    assert lib.gdn_decode_step(ctypes.byref(sh), 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, FAKE, None,
+                               FAKE, None) == 1
+    assert lib.gdn_decode_step(ctypes.byref(sh), 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, 5, None, None,
+                               FAKE, None) == 1
+
+
+@no_gpu
+def test_snapshot_and_conv_validation_errors():
+    lib = gdn.load()
+    sl = np.array([0, 2, 2], np.int64)
+    assert lib.gdn_snapshot_copy(FAKE, 3, 64, FAKE, 4, FAKE, sl.ctypes.data, None, None, None) == 6
+    sl = np.array([0, 2, 4], np.int64)
+    assert lib.gdn_snapshot_copy(FAKE, 3, 64, FAKE, 4, FAKE, sl.ctypes.data, None, None, None) == 6
+    sl = np.array([0, 2, 3], np.int64)
+    assert lib.gdn_snapshot_copy(FAKE, 3, 60, FAKE, 4, FAKE, sl.ctypes.data, None, None, None) == 2
+    assert lib.gdn_snapshot_copy(FAKE, 3, 64, None, 4, FAKE, sl.ctypes.data, None, None, None) == 1
+    assert lib.gdn_snapshot_copy(FAKE, 0, 64, None, 4, None, None, None, None, None) == 0
+    sh = gdn.make_shape(2, 2, 32, 32, 16, gdn.GDN_F32)
+    cu = np.array([0, 40, 64], np.int32)
+    # y overlapping x
+    assert lib.gdn_conv1d_silu_packed(ctypes.byref(sh), FAKE, cu.ctypes.data, 2, 64, FAKE, 0, FAKE, None,
+                                      FAKE + 192 * 4, 0, None, None, None, 0, None, None) == 2
+    bad = np.array([0, 40, 63], np.int32)
+    assert lib.gdn_conv1d_silu_packed(ctypes.byref(sh), FAKE, bad.ctypes.data, 2, 64, FAKE, 0, FAKE, None,
+                                      FAKE * 64, 0, None, None, None, 0, None, None) == 4
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(gdn, "_lib", None)
+    monkeypatch.setattr(gdn, "LIB_PATH", "/nonexistent/libgdn.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        gdn.load()

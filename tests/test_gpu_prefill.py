@@ -1,0 +1,155 @@
+"""GPU parity of gdn_prefill_packed against the fp64 oracle, through the C ABI.
+
+Tolerances: states and checkpoints 1e-3 relative Frobenius per (sequence or
+checkpoint, head); outputs max-relative per (token, head) row 2e-2 for bf16,
+1e-3 for fp32; checkpoint positions and packed-vs-alone results bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_prefill_varlen_amd as gdn
+import oracle as O
+import workloads as W
+from gpu_util import (DevPack, all_pairs, assert_parity, sample_pairs, shape_of, to_f64,
+                      io_tensor, f32_tensor, i32_tensor, DEV)
+
+pytestmark = pytest.mark.gpu
+
+
+def _ckpt(p, block=None):
+    return gdn.gdn_plan_checkpoints(p.cu_seqlens, block or p.block)
+
+
+def test_tiny_pack_fp32():
+    p = W.tiny_pack()
+    ck = _ckpt(p)
+    assert list(ck) == [16]
+    dp = DevPack(p, ck).run()
+    torch.cuda.synchronize()
+    eo, es = assert_parity(dp, all_pairs(p))
+    print(f"tiny fp32: out {eo:.2e} state {es:.2e}")
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 64), (128, 128)])
+def test_every_residue_bf16(dk, dv):
+    p = W.make_pack("residue", list(range(1, 131)), 2, 4, dk, dv, 16, 16, seed=dk + dv, init_std=0.1)
+    dp = DevPack(p, _ckpt(p)).run()
+    torch.cuda.synchronize()
+    assert_parity(dp, sample_pairs(p, 60, seed=dk))
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunk_sizes_and_slow_decay(chunk):
+    p = W.make_pack("slow", [200, 64, 129, 1, 300], 2, 4, 128, 128, chunk, 64, seed=chunk,
+                    init_std=0.1, gate_scale=0.01)
+    dp = DevPack(p, _ckpt(p, 64)).run()
+    torch.cuda.synchronize()
+    assert_parity(dp, all_pairs(p))
+
+
+def test_unnormalised_qk_and_scale():
+    p = W.make_pack("raw", [77, 190], 2, 4, 128, 128, 64, 64, seed=5, init_std=0.1, unit_qk=False,
+                    scale=128 ** -0.5)
+    dp = DevPack(p, _ckpt(p)).run()
+    torch.cuda.synchronize()
+    assert_parity(dp, all_pairs(p))
+
+
+def test_strided_views_of_one_row():
+    """q, k, v as column views of one [T, conv_dim] tensor (token strides)."""
+    p = W.make_pack("views", [100, 37], 2, 4, 64, 64, 32, 32, seed=9, init_std=0.1)
+    T = p.n_tokens
+    row = np.concatenate([p.q.reshape(T, -1), p.k.reshape(T, -1), p.v.reshape(T, -1)], axis=1)
+    big = io_tensor(row, "bf16")
+    nq = p.Hqk * p.dk
+    dp = DevPack(p, _ckpt(p))
+    dp.q, dp.k, dp.v = big[:, :nq], big[:, nq:2 * nq], big[:, 2 * nq:]
+    cd = row.shape[1]
+    dp.run(shape_of(p, q_tok_stride=cd, k_tok_stride=cd, v_tok_stride=cd))
+    torch.cuda.synchronize()
+    assert_parity(dp, all_pairs(p))
+
+
+def test_empty_prompts_keep_their_state():
+    p = W.make_pack("empty", [0, 50, 0, 0, 70, 0], 2, 4, 32, 32, 16, 16, seed=3, init_std=0.1)
+    dp = DevPack(p, _ckpt(p)).run()
+    torch.cuda.synchronize()
+    fin = to_f64(dp.final)
+    for s in (0, 2, 3, 5):
+        np.testing.assert_array_equal(fin[s], p.init[s].astype(np.float64))
+    assert_parity(dp, all_pairs(p))
+
+
+def test_zero_init_equals_null_init():
+    p = W.make_pack("z", [90, 33], 2, 4, 64, 64, 32, 32, seed=4)
+    a = DevPack(p, _ckpt(p)).run()
+    p.init = np.zeros((p.n_seqs, p.Hv, p.dv, p.dk), np.float32)
+    b = DevPack(p, _ckpt(p)).run()
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, b.out) and torch.equal(a.final, b.final)
+
+
+def test_deterministic_run_twice():
+    p = W.ragged_pack(seed=2)
+    dp = DevPack(p, _ckpt(p)).run()
+    o1, f1, c1 = dp.out.clone(), dp.final.clone(), dp.ckpt_buf.clone()
+    dp.run()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, dp.out) and torch.equal(f1, dp.final) and torch.equal(c1, dp.ckpt_buf)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_ragged_packed_equals_alone_bitwise(seed):
+    """Checkpoints, outputs and final states are bit-identical whether each
+    prompt is prefilled alone or packed (the pages' alone-vs-packed check)."""
+    p = W.ragged_pack(seed=seed)
+    ck = _ckpt(p)
+    np.testing.assert_array_equal(ck, O.plan_checkpoints(p.cu_seqlens, p.block))
+    dp = DevPack(p, ck).run()
+    torch.cuda.synchronize()
+    for s in range(p.n_seqs):
+        c0, c1 = int(p.cu_seqlens[s]), int(p.cu_seqlens[s + 1])
+        sub = W.Pack(name="alone", cu_seqlens=np.array([0, c1 - c0], np.int32), Hqk=p.Hqk, Hv=p.Hv,
+                     dk=p.dk, dv=p.dv, chunk=p.chunk, block=p.block, dtype=p.dtype,
+                     q=p.q[c0:c1], k=p.k[c0:c1], v=p.v[c0:c1], g=p.g[c0:c1], beta=p.beta[c0:c1],
+                     init=p.init[s:s + 1])
+        mine = [int(x) - c0 for x in ck if c0 < x <= c1]
+        alone = DevPack(sub, mine).run()
+        torch.cuda.synchronize()
+        assert torch.equal(alone.out, dp.out[c0:c1])
+        assert torch.equal(alone.final[0], dp.final[s])
+        idx = [i for i, x in enumerate(ck) if c0 < x <= c1]
+        if idx:
+            assert torch.equal(alone.ckpt_buf, dp.ckpt_buf[idx])
+    assert_parity(dp, sample_pairs(p, 24, seed=seed))
+
+
+@pytest.mark.slow
+def test_chat_wave_full_size_sampled():
+    p = W.chat_wave()
+    ck = _ckpt(p)
+    assert len(ck) == 96
+    dp = DevPack(p, ck).run()
+    torch.cuda.synchronize()
+    eo, es = assert_parity(dp, sample_pairs(p, 8))
+    print(f"chat wave: out {eo:.2e} state {es:.2e}")
+
+
+@pytest.mark.slow
+def test_long_prompts_full_size_sampled():
+    p = W.long_prompts()
+    ck = _ckpt(p)
+    assert len(ck) == 28
+    dp = DevPack(p, ck).run()
+    torch.cuda.synchronize()
+    eo, es = assert_parity(dp, sample_pairs(p, 3, seed=4))
+    print(f"long prompts: out {eo:.2e} state {es:.2e}")
+
+
+def test_slow_decay_ragged_init_visible():
+    """With slow decay the initial state still shapes the final state, so a
+    dropped or misplaced init would fail here (it need not at fast decay)."""
+    p = W.slow_decay(W.ragged_pack, seed=3)
+    dp = DevPack(p, _ckpt(p)).run()
+    torch.cuda.synchronize()
+    assert_parity(dp, sample_pairs(p, 12, seed=3))
