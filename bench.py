@@ -1,0 +1,363 @@
+"""Benchmark: packed gated-delta-rule prefill tokens/s per layer on one MI355X.
+
+Default workload: a chat wave of 32 prompts x 1,024 tokens packed into one
+pass (16 qk / 32 v heads, d = 128, bf16 q/k/v, fp32 gates and state, chunk
+64, checkpoint every 256 tokens).  A step is one gdn_prefill_packed call on
+that pack (the chunked scan with its checkpoint writes to device memory),
+with the inputs resident in HBM.  The other rows of the path are timed in the
+same run as legs: the conv at the same shape, the checkpoint copy on its own
+stream, the decode batch and the mixed pass, and the long-prompt and ragged
+packs.
+
+Prints ONE JSON line on stdout.  ``--gpus N`` with N > 1 exits: this build
+runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------- algorithmic work --
+
+def prefill_alg_bytes(p, n_ckpt: int, init_nonzero: bool) -> int:
+    """Bytes the method must move: q, k, v, g, beta in, out out, the final
+    state per prompt (+ the initial state when given), and each checkpoint."""
+    e = 2 if p.dtype == "bf16" else 4
+    per_tok = (2 * p.Hqk * p.dk + p.Hv * p.dv) * e + 2 * p.Hv * 4 + p.Hv * p.dv * e
+    state = p.Hv * p.dv * p.dk * 4
+    return p.n_tokens * per_tok + p.n_seqs * state * (2 if init_nonzero else 1) + n_ckpt * state
+
+
+def prefill_alg_flops(p) -> float:
+    """Chunked form, per token per value head: 2C(3dk + 2dv) + 6 dk dv + C^2/3."""
+    C, dk, dv = p.chunk, p.dk, p.dv
+    return p.n_tokens * p.Hv * (2 * C * (3 * dk + 2 * dv) + 6 * dk * dv + C * C / 3)
+
+
+# --------------------------------------------------------------- GPU legs --
+
+class Timer:
+    """HIP events on one stream around each launch; returns per-launch ms."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def run(self, fn, reps: int, flush=None):
+        t = self.torch
+        times = []
+        for _ in range(reps):
+            if flush is not None:
+                with t.cuda.stream(self.stream):
+                    flush()
+            a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        return times
+
+
+def make_flush(torch, dev):
+    buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB > 256 MB MALL
+
+    def flush():
+        buf.fill_(1.0)
+    return flush
+
+
+def io_t(torch, a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+
+
+def f32_t(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+
+
+def i32_t(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda:0")
+
+
+class DevPack:
+    """A pack resident in HBM with its output buffers; ``run`` is one
+    gdn_prefill_packed call."""
+
+    def __init__(self, torch, gdn, p, ck):
+        self.gdn, self.p = gdn, p
+        self.ck = np.asarray(ck, dtype=np.int32)
+        self.cu = i32_t(torch, p.cu_seqlens)
+        self.q, self.k, self.v = (io_t(torch, a, p.dtype) for a in (p.q, p.k, p.v))
+        self.g, self.beta = f32_t(torch, p.g), f32_t(torch, p.beta)
+        self.init = None if p.init is None else f32_t(torch, p.init)
+        self.ck_d = i32_t(torch, self.ck) if len(self.ck) else None
+        odt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+        self.out = torch.empty((p.n_tokens, p.Hv, p.dv), dtype=odt, device="cuda:0")
+        self.final = torch.empty((p.n_seqs, p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
+        self.ckbuf = (torch.empty((len(self.ck), p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
+                      if len(self.ck) else None)
+        self.shape = gdn.make_shape(p.Hqk, p.Hv, p.dk, p.dv, p.chunk,
+                                    gdn.GDN_BF16 if p.dtype == "bf16" else gdn.GDN_F32, scale=p.scale)
+
+    def run(self, stream=None):
+        self.gdn.gdn_prefill_packed(self.shape, self.cu, self.p.cu_seqlens, self.q, self.k, self.v,
+                                    self.g, self.beta, self.init, self.ck_d,
+                                    self.ck if len(self.ck) else None, self.out, self.final, self.ckbuf,
+                                    stream=stream)
+
+
+def bench_prefill(torch, gdn, p, steps, warmup, stream, flush, label):
+    ck = gdn.gdn_plan_checkpoints(p.cu_seqlens, p.block)
+    dp = DevPack(torch, gdn, p, ck)
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            dp.run(stream=stream)
+        torch.cuda.synchronize()
+        times = Timer(torch, stream).run(lambda: dp.run(stream=stream), steps, flush)
+    torch.cuda.synchronize()
+    med = statistics.median(times)
+    B = prefill_alg_bytes(p, len(ck), p.init is not None)
+    F = prefill_alg_flops(p)
+    t_roof = max(B / (HBM_PEAK_GBS * 1e9), F / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    res = {
+        "workload": label, "tokens": p.n_tokens, "prompts": p.n_seqs, "checkpoints": int(len(ck)),
+        "ms_median": med, "ms_p10": float(np.percentile(times, 10)), "ms_p90": float(np.percentile(times, 90)),
+        "tokens_per_s": p.n_tokens / (med * 1e-3), "alg_bytes": B, "alg_flops": F,
+        "achieved_GBs": B / (med * 1e-3) / 1e9, "roofline_frac": t_roof / (med * 1e-3),
+    }
+    del dp
+    return res, times
+
+
+def bench_conv(torch, gdn, stream, flush, reps):
+    T, Hqk, Hv, d = 32768, 16, 32, 128
+    C = 2 * Hqk * d + Hv * d
+    cu = np.arange(0, T + 1, 1024, dtype=np.int32)
+    x = torch.randn((T, C), device="cuda:0").to(torch.bfloat16)
+    w = torch.randn((C, 4), device="cuda:0") * 0.5
+    y = torch.empty_like(x)
+    st = torch.empty((len(cu) - 1, 3, C), dtype=torch.bfloat16, device="cuda:0")
+    shape = gdn.make_shape(Hqk, Hv, d, d, 64)
+    cu_d = i32_t(torch, cu)
+    fn = lambda: gdn.gdn_conv1d_silu_packed(shape, cu_d, cu, x, w, y, None, st, stream=stream)
+    fn()
+    times = Timer(torch, stream).run(fn, reps, flush)
+    med = statistics.median(times)
+    B = 2 * T * C * 2 + st.numel() * 2 + w.numel() * 4
+    return {"workload": "conv1d_silu 32x1024 tokens x 8192 ch bf16", "ms_median": med,
+            "achieved_GBs": B / (med * 1e-3) / 1e9, "roofline_frac": B / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_snapshot(torch, gdn, stream, flush, reps):
+    n, Hv, d = 96, 32, 128
+    src = torch.randn((n, Hv, d, d), device="cuda:0")
+    pool = torch.empty((n + 32, Hv, d, d), device="cuda:0")
+    slots = np.random.default_rng(0).permutation(n + 32)[:n].astype(np.int64)
+    slots_d = torch.from_numpy(slots).to("cuda:0")
+    each = Hv * d * d * 4
+    fn = lambda: gdn.gdn_snapshot_copy(src, n, each, pool, slots_d, slots, n + 32, copy_stream=stream)
+    fn()
+    times = Timer(torch, stream).run(fn, reps, flush)
+    med = statistics.median(times)
+    B = 2 * n * each
+    ok = bool(torch.equal(pool[slots_d], src))
+    return {"workload": "checkpoint copy 96 x 2 MiB device pool", "ms_median": med,
+            "achieved_GBs": B / (med * 1e-3) / 1e9, "roofline_frac": B / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "exact": ok}
+
+
+def bench_decode(torch, gdn, stream, flush, reps):
+    import workloads as W
+    d = W.decode_batch(seed=0, batch=32, pool=64)
+    q, k, v = (io_t(torch, a, "bf16") for a in (d.q, d.k, d.v))
+    g, b = f32_t(torch, d.g), f32_t(torch, d.beta)
+    st = f32_t(torch, d.state)
+    slot = i32_t(torch, d.slot)
+    out = torch.empty((32, 32, 128), dtype=torch.bfloat16, device="cuda:0")
+    shape = gdn.make_shape(16, 32, 128, 128, 64)
+    fn = lambda: gdn.gdn_decode_step(shape, q, k, v, g, b, st, slot, d.slot, out, stream=stream)
+    fn()
+    times = Timer(torch, stream).run(fn, reps, flush)
+    med = statistics.median(times)
+    B = 32 * 32 * 128 * 128 * 4 * 2 + 32 * (2 * 16 * 128 * 2 + 32 * 128 * 2 * 2 + 32 * 8)
+    return {"workload": "decode 32 seqs x 32 heads, fp32 state in place", "ms_median": med,
+            "achieved_GBs": B / (med * 1e-3) / 1e9, "roofline_frac": B / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_mixed(torch, gdn, stream, flush, reps):
+    import workloads as W
+    pack, d = W.mixed_step(seed=0)
+    dp = DevPack(torch, gdn, pack, [])
+    q, k, v = (io_t(torch, a, "bf16") for a in (d.q, d.k, d.v))
+    g, b = f32_t(torch, d.g), f32_t(torch, d.beta)
+    st, slot = f32_t(torch, d.state), i32_t(torch, d.slot)
+    out = torch.empty((32, 32, 128), dtype=torch.bfloat16, device="cuda:0")
+    shape = gdn.make_shape(16, 32, 128, 128, 64)
+
+    def fn():
+        dp.run(stream=stream)
+        gdn.gdn_decode_step(shape, q, k, v, g, b, st, slot, d.slot, out, stream=stream)
+    fn()
+    times = Timer(torch, stream).run(fn, reps, flush)
+    med = statistics.median(times)
+    toks = pack.n_tokens + d.batch
+    return {"workload": f"mixed pass: {pack.n_tokens} prefill tokens ({pack.n_seqs} prompts) + 32 decodes",
+            "ms_median": med, "tokens_per_s": toks / (med * 1e-3)}
+
+
+# ------------------------------------------------------------ CPU oracle --
+
+def _oracle_one_prompt(args):
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        import oracle as O
+        q, k, v, g, b = args
+        t = time.perf_counter()
+        O.prefill_recurrent(q, k, v, g, b, [0, q.shape[0]])
+        return time.perf_counter() - t
+
+
+def cpu_baseline(p, n_prompts: int):
+    """The fp64 oracle, untouched, on the first n_prompts prompts of the pack,
+    one process per prompt (one BLAS thread each)."""
+    import oracle as O
+    cores = len(os.sched_getaffinity(0))
+    procs = min(cores, n_prompts)
+    jobs = []
+    for s in range(n_prompts):
+        sl = slice(int(p.cu_seqlens[s]), int(p.cu_seqlens[s + 1]))
+        jobs.append((O.to_f64(p.q[sl], p.dtype), O.to_f64(p.k[sl], p.dtype), O.to_f64(p.v[sl], p.dtype),
+                     p.g[sl].astype(np.float64), p.beta[sl].astype(np.float64)))
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(procs) as pool:
+        per = pool.map(_oracle_one_prompt, jobs)
+    wall = time.perf_counter() - t0
+    toks = sum(j[0].shape[0] for j in jobs)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": toks / wall, "unit": "tokens/s/layer", "cores": procs, "kind": "oracle",
+            "sample": f"{n_prompts} of the 32 prompts ({toks} tokens, all 32 heads), fp64 token-by-token "
+                      f"recurrence, one process per prompt; wall {wall:.1f} s; {cpu_model}",
+            "cpu_seconds": float(sum(per))}
+
+
+# ------------------------------------------------------------------ main --
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-legs", action="store_true", help="time only the headline step")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-prompts", type=int, default=8)
+    ap.add_argument("--workload", default="chat", choices=["chat", "long", "ragged"])
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on exactly one GPU (the path shards by value-head groups "
+              "with no exchange; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_prefill_varlen_amd as gdn
+    import workloads as W
+
+    gdn.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    flush = make_flush(torch, dev)
+
+    makers = {"chat": (W.chat_wave, "chat wave 32 x 1,024 tokens"),
+              "long": (W.long_prompts, "long prompts 4 x 8,192 tokens"),
+              "ragged": (W.ragged_pack, "ragged 8 prompts <= 8,192 tokens, prefix-cache init")}
+    fn, label = makers[args.workload]
+    log(f"[bench] generating {label}")
+    p = fn(seed=0)
+    log("[bench] timing headline step")
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    head, times = bench_prefill(torch, gdn, p, args.steps, args.warmup, stream, flush, label)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    log(f"[bench] headline: {head['ms_median']:.3f} ms, {head['tokens_per_s']/1e6:.2f} M tok/s, "
+        f"{head['roofline_frac']*100:.1f}% of roofline")
+
+    legs = {}
+    if not args.no_legs:
+        for name, f in (("conv", bench_conv), ("snapshot_copy", bench_snapshot), ("decode", bench_decode),
+                        ("mixed", bench_mixed)):
+            log(f"[bench] leg {name}")
+            legs[name] = f(torch, gdn, stream, flush, 10)
+        for wname in ("long", "ragged"):
+            if wname == args.workload:
+                continue
+            log(f"[bench] leg {wname}")
+            wp = makers[wname][0](seed=0)
+            legs[wname], _ = bench_prefill(torch, gdn, wp, 5, 1, stream, flush, makers[wname][1])
+            del wp
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(p, args.cpu_prompts)
+
+    med_s = head["ms_median"] * 1e-3
+    line = {
+        "metric": "packed GDN prefill tokens/s/layer (32x1K pack) + % of MFMA/HBM roofline",
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_median"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in/out, fp32 state and accumulation",
+        "data": "synthetic (seeded; shapes of the pages' chat waves)",
+        "config": {"workload": head["workload"], "tokens": p.n_tokens, "prompts": p.n_seqs,
+                   "qk_heads": p.Hqk, "v_heads": p.Hv, "head_dim": p.dk, "chunk": p.chunk,
+                   "checkpoint_block": p.block, "checkpoints": head["checkpoints"],
+                   "timing": "median of per-step HIP-event times on the launch stream; 1 GiB cache "
+                             "flush before each step, outside the events",
+                   "wall_s_timed_region": t_wall},
+        "roofline": {"bound": "hbm", "achieved": head["achieved_GBs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": head["achieved_GBs"] / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gdn prefill scan", "alg_bytes_per_launch": head["alg_bytes"],
+                     "mfma_alg_tflops": head["alg_flops"] / med_s / 1e12},
+        "cpu_baseline": cpu,
+        "legs": legs,
+        "step_ms_p10_p90": [head["ms_p10"], head["ms_p90"]],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,4 @@
+// Chunked prefill kernels for head_k_dim = 32.
+#include "scan_chunked_kernel.h"
+
+GDN_CHUNKED_LAUNCHERS(32)
