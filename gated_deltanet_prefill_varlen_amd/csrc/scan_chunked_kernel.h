@@ -13,21 +13,22 @@
 // Networks, ICLR 2025.)  The L2 norms enter only as fp32 row scalings, so the
 // raw bf16 q/k/v are exact MFMA operands.
 //
-// Work split inside the workgroup (DV/32 waves): all waves stage K, K^T and
-// Q of the chunk in LDS and compute the Gram and Q K^T tiles; wave 0 inverts
-// the 32x32 diagonal blocks of (I + A) by forward substitution (the
-// off-diagonal block is applied to Y directly: U1 = T11 Y1,
-// U2 = T22 (Y2 - A21 U1), so T21 is never formed); then wave w owns state columns
+// Work split (DV/32 waves): all waves stage K and Q of the chunk in LDS and
+// share the Gram / Q K^T tiles and the inversion of the 32x32 diagonal blocks
+// of (I + A) (forward substitution, several lanes per column); the
+// off-diagonal block is applied to Y directly, U1 = T11 Y1,
+// U2 = T22 (Y2 - A21 U1), so T21 is never formed.  Wave w owns state columns
 // v in [32w, 32w+32): its slice of S stays in MFMA accumulator registers for
 // the whole prompt (fp32), laid out as S^T tiles (rows k, lane column v).
+// LDS is kept under 80 KB and registers under 256 so two workgroups share a
+// CU and overlap each other's latency-bound phases.
 //
-// Precision: products that carry fp32 quantities into the state use split
-// bf16 operands (x = hi + lo, hi = bf16(x), lo = bf16(x - hi); the lo*lo pass
-// is dropped): K S0^T with S0 split (2 passes), T Y with T and Y split (3
-// passes, likewise A21 U1), K^T U' with U' split (2 passes).  The output
-// products are split too (Q S0^T: 2 passes; P U with P and U split: 3): a
-// dot of a unit q with a state row is ~1/sqrt(dk) of |q||S row| while single
-// bf16 rounding errors are not, which costs ~1e-2 relative on outputs.
+// Precision: every product that carries fp32 values uses split bf16 operands
+// (x = hi + lo, hi = bf16(x), lo = bf16(x - hi); the lo*lo pass dropped):
+// K S0^T and Q S0^T with S0 split (2 passes), T Y, A21 U1, P U with both
+// sides split (3 passes), K^T U' with U' split (2 passes).  A dot of a unit q
+// with a state row is ~1/sqrt(dk) of |q||S row| while single bf16 rounding
+// errors are not, which is why the output products are split too.
 // Accumulation is fp32 throughout.
 #pragma once
 
@@ -51,23 +52,17 @@ __device__ __forceinline__ f32x16 mma(const bf16x8& a, const bf16x8& b, const f3
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// MFMA A operand from a bf16 row in LDS.  The k order used across every
-// product: within a 16-wide k step at offset 16*h2, lane half g (= l/32) holds
+// MFMA operand from a bf16 row in LDS.  The k order used by every product:
+// within a 16-wide k step at offset 16*h2, lane half g (= l/32) holds
 // k = 16*h2 + 4g + {0,1,2,3} and 16*h2 + 8 + 4g + {0,1,2,3}; this is exactly
 // the row order of accumulator registers 8*h2 .. 8*h2+7, so an accumulator
 // tile feeds the next product as its B operand without moving data.
-// `p` points at element 16*h2 + 4g of the row.
-__device__ __forceinline__ bf16x8 lds_a(const uint16_t* p) {
+// `p` points at element 16*h2 + 4g of the row (8-byte aligned).
+__device__ __forceinline__ bf16x8 lds_op(const uint16_t* p) {
   const u32x2 a = *reinterpret_cast<const u32x2*>(p);
   const u32x2 b = *reinterpret_cast<const u32x2*>(p + 8);
   const u32x4 v = {a.x, a.y, b.x, b.y};
   return __builtin_bit_cast(bf16x8, v);
-}
-
-// Eight consecutive bf16 of a row (natural k order; both operands of a
-// product read with it, so the order cancels).
-__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
 // Accumulator half h2 (registers 8h2..8h2+7) as a B operand, split into
@@ -82,16 +77,13 @@ __device__ __forceinline__ void split_half(const f32x16& x, bf16x8& hi, bf16x8& 
     lo[j] = (__bf16)(f - (float)h);
   }
 }
-template <int H2>
-__device__ __forceinline__ bf16x8 hi_half(const f32x16& x) {
-  bf16x8 hi;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) hi[j] = (__bf16)x[8 * H2 + j];
-  return hi;
-}
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) {
-  return __builtin_bit_cast(uint16_t, (__bf16)f);
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+__device__ __forceinline__ void store_split(uint16_t* hi_plane, int plane_stride, int idx, float x) {
+  const __bf16 h = (__bf16)x;
+  hi_plane[idx] = __builtin_bit_cast(uint16_t, h);
+  hi_plane[plane_stride + idx] = bf16_bits(x - (float)h);
 }
 
 // Row of accumulator register i for lane half g.
@@ -103,33 +95,37 @@ struct Cfg {
   static constexpr int NW = DV / 32;      // waves
   static constexpr int NTH = 64 * NW;     // threads
   static constexpr int KT = DK / 32;      // 32-wide k tiles of the state
-  static constexpr int LDK = DK + 8;      // row stride of sK, sQ (bf16)
-  static constexpr int LDT = CT + 8;      // row stride of sKT, sT, sP (bf16)
-  static constexpr int LDA = 36;          // row stride of sA (fp32 diagonal 32x32 blocks)
+  static constexpr int LDK = DK + 4;      // row stride of sK, sQ (bf16; 8-byte aligned rows)
+  static constexpr int LDT = CT + 4;      // row stride of sT, sP (bf16)
+  // forward substitution: LPC lanes per column of the diagonal blocks
+  static constexpr int LPC_RAW = NTH / CT;
+  static constexpr int LPC = LPC_RAW > 8 ? 8 : (LPC_RAW < 1 ? 1 : LPC_RAW);
+  static constexpr int MPL = 32 / LPC;    // rows of a column held per lane
+  static constexpr int LDA = 32 + 4;      // row stride of a diagonal block of A (fp32)
   static constexpr int oK = 0;
   static constexpr int oQ = oK + CT * LDK * 2;
-  static constexpr int oKT = oQ + CT * LDK * 2;
-  static constexpr int oT = oKT + DK * LDT * 2;       // hi then lo: T11, -A21, T22
-  static constexpr int oP = oT + 2 * CT * LDT * 2;
-  static constexpr int oA = oP + 2 * CT * LDT * 2;    // P hi then lo
-  static constexpr int oS = oA + CT * LDA * 4;        // per-token scalars (A: NT diagonal blocks)
+  static constexpr int oT = oQ + CT * LDK * 2;        // hi then lo plane: T11, -A21, T22
+  static constexpr int oP = oT + 2 * CT * LDT * 2;    // hi then lo plane
+  static constexpr int oA = oP + 2 * CT * LDT * 2;    // NT diagonal blocks of A, lane-interleaved
+  static constexpr int oS = oA + NT * 32 * LDA * 4;   // per-token scalars
   static constexpr int kScal = 8;
   static constexpr int bytes = oS + kScal * CT * 4;
-  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert(bytes <= 80 * 1024, "two workgroups per CU");
+  static_assert(LPC * CT <= NTH || LPC == 1, "substitution lanes");
 };
 
 // per-token scalar arrays (index into the scalar block)
-enum { SC_G = 0, SC_BETA, SC_RK, SC_RQ, SC_CUM, SC_CK, SC_CQ, SC_CU };
+enum { SC_G = 0, SC_BETA, SC_RK, SC_RQ, SC_CK, SC_CQ, SC_CU, SC_PAD };
 
 template <int DK, int DV, int NT>
-__global__ void __launch_bounds__(64 * (DV / 32))
+__global__ void __launch_bounds__(64 * (DV / 32), 2)
 chunked_prefill_kernel(const ScanArgs a) {
   using C = Cfg<DK, DV, NT>;
   constexpr int CT = C::CT, NTH = C::NTH, KT = C::KT, LDK = C::LDK, LDT = C::LDT, LDA = C::LDA;
+  constexpr int LPC = C::LPC, MPL = C::MPL;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* sK = reinterpret_cast<uint16_t*>(smem + C::oK);
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + C::oQ);
-  uint16_t* sKT = reinterpret_cast<uint16_t*>(smem + C::oKT);
   uint16_t* sT = reinterpret_cast<uint16_t*>(smem + C::oT);
   uint16_t* sP = reinterpret_cast<uint16_t*>(smem + C::oP);
   float* sA = reinterpret_cast<float*>(smem + C::oA);
@@ -141,6 +137,7 @@ chunked_prefill_kernel(const ScanArgs a) {
   float* sCk = sc + SC_CK * CT;     // r_k e^G
   float* sCq = sc + SC_CQ * CT;     // scale r_q e^G
   float* sCu = sc + SC_CU * CT;     // r_k e^{G_C - G}
+  constexpr int TPL = CT * LDT;     // bf16 elements per hi/lo plane
 
   const int s = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -149,8 +146,8 @@ chunked_prefill_kernel(const ScanArgs a) {
   const int seq0 = a.cu[s], seq1 = a.cu[s + 1];
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
   const uint16_t* kg = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v);
-  uint16_t* og = static_cast<uint16_t*>(a.out);
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)h * DV;
+  uint16_t* og = static_cast<uint16_t*>(a.out) + (size_t)h * DV;
   const size_t sstride = (size_t)a.Hv * DV * DK;
   const int v = 32 * wave + c;       // this lane's state column (value dim)
 
@@ -192,8 +189,10 @@ chunked_prefill_kernel(const ScanArgs a) {
         kv = *reinterpret_cast<const u32x4*>(kg + (size_t)(t0 + t) * a.k_stride + (size_t)j * DK + c8);
         qv = *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + t) * a.q_stride + (size_t)j * DK + c8);
       }
-      *reinterpret_cast<u32x4*>(sK + t * LDK + c8) = kv;
-      *reinterpret_cast<u32x4*>(sQ + t * LDK + c8) = qv;
+      u32x2* kd = reinterpret_cast<u32x2*>(sK + t * LDK + c8);
+      u32x2* qd = reinterpret_cast<u32x2*>(sQ + t * LDK + c8);
+      kd[0] = u32x2{kv.x, kv.y}; kd[1] = u32x2{kv.z, kv.w};
+      qd[0] = u32x2{qv.x, qv.y}; qd[1] = u32x2{qv.z, qv.w};
     }
     if (tid < CT) {
       const bool ok = tid < n;
@@ -202,19 +201,9 @@ chunked_prefill_kernel(const ScanArgs a) {
     }
     __syncthreads();
 
-    // ---- 2. K^T, row norms, gate cumsum
-    for (int e = tid; e < DK * CT / 8; e += NTH) {
-      const int k = e % DK, t8 = (e / DK) * 8;
-      uint32_t w[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        w[p] = (uint32_t)sK[(t8 + 2 * p) * LDK + k] | ((uint32_t)sK[(t8 + 2 * p + 1) * LDK + k] << 16);
-      const u32x4 wv = {w[0], w[1], w[2], w[3]};
-      *reinterpret_cast<u32x4*>(sKT + k * LDT + t8) = wv;
-    }
+    // ---- 2. row norms, gate cumsum
     {
-      // row norms: TPR consecutive lanes per row, at least 8 columns each
-      constexpr int TPR_RAW = NTH / CT >= 1 ? NTH / CT : 1;
+      constexpr int TPR_RAW = NTH / CT >= 1 ? NTH / CT : 1;   // lanes per row
       constexpr int TPR = TPR_RAW < DK / 8 ? TPR_RAW : DK / 8;
       constexpr int PER = DK / TPR;
       constexpr int RPP = NTH / TPR;  // rows per pass
@@ -226,13 +215,13 @@ chunked_prefill_kernel(const ScanArgs a) {
         const int part = tid % TPR;
         float sk = 0.f, sq = 0.f;
 #pragma unroll
-        for (int e = 0; e < PER; e += 8) {
+        for (int e = 0; e < PER; e += 4) {
           const int col = part * PER + e;
-          const u32x4 kk = *reinterpret_cast<const u32x4*>(sK + tt * LDK + col);
-          const u32x4 qq = *reinterpret_cast<const u32x4*>(sQ + tt * LDK + col);
-          const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w}, qw[4] = {qq.x, qq.y, qq.z, qq.w};
+          const u32x2 kk = *reinterpret_cast<const u32x2*>(sK + tt * LDK + col);
+          const u32x2 qq = *reinterpret_cast<const u32x2*>(sQ + tt * LDK + col);
+          const uint32_t kw[2] = {kk.x, kk.y}, qw[2] = {qq.x, qq.y};
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
+          for (int p = 0; p < 2; ++p) {
             const float k0 = bf16_to_f32(kw[p] & 0xFFFFu), k1 = bf16_to_f32(kw[p] >> 16);
             const float q0 = bf16_to_f32(qw[p] & 0xFFFFu), q1 = bf16_to_f32(qw[p] >> 16);
             sk = fmaf(k0, k0, sk); sk = fmaf(k1, k1, sk);
@@ -259,41 +248,43 @@ chunked_prefill_kernel(const ScanArgs a) {
     }
     __syncthreads();
 
-    // ---- 3. Gram and Q K^T tiles (MFMA) -> A (fp32) and P (bf16); per-token scalars
+    // ---- 3. Gram and Q K^T tiles (MFMA, shared K operand) -> A, P; scalars
     {
       constexpr int NTILE = NT * (NT + 1) / 2;
-      for (int job = wave; job < 2 * NTILE; job += C::NW) {
-        const bool gram = job < NTILE;
-        const int tix = gram ? job : job - NTILE;
+      for (int tix = wave; tix < NTILE; tix += C::NW) {
         const int mt = tix == 0 ? 0 : 1, nt = tix == 2 ? 1 : 0;
-        const uint16_t* ap = (gram ? sK : sQ) + (32 * mt + c) * LDK + 8 * g;
-        const uint16_t* bp = sK + (32 * nt + c) * LDK + 8 * g;
-        f32x16 acc = {};
+        const uint16_t* kr = sK + (32 * mt + c) * LDK + 4 * g;
+        const uint16_t* qr = sQ + (32 * mt + c) * LDK + 4 * g;
+        const uint16_t* br = sK + (32 * nt + c) * LDK + 4 * g;
+        f32x16 gk = {}, gq = {};
 #pragma unroll
-        for (int ks = 0; ks < DK / 16; ++ks) acc = mma(lds_row8(ap + 16 * ks), lds_row8(bp + 16 * ks), acc);
-        const int col = 32 * nt + c;
+        for (int ks = 0; ks < DK / 16; ++ks) {
+          const bf16x8 b = lds_op(br + 16 * ks);
+          gk = mma(lds_op(kr + 16 * ks), b, gk);
+          gq = mma(lds_op(qr + 16 * ks), b, gq);
+        }
+        const int col = 32 * nt + c, lcol = c;   // global / block-local column
         const float gc = sG[col], rkc = sRk[col];
+        const int qa = lcol % LPC, ma = lcol / LPC;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = 32 * mt + acc_row(i, g);
-          if (gram) {
-            const bool lower = col < t;
-            const float dcy = __expf(lower ? sG[t] - gc : 0.f);
-            const float av = lower ? sBeta[t] * sRk[t] * rkc * dcy * acc[i] : 0.f;
-            if (mt == nt) {
-              sA[t * LDA + (col - 32 * nt)] = av;           // diagonal block, fp32
-            } else {                                        // -A21 as hi/lo bf16 operand
-              const __bf16 hi = (__bf16)(-av);
-              sT[t * LDT + col] = __builtin_bit_cast(uint16_t, hi);
-              sT[CT * LDT + t * LDT + col] = bf16_bits(-av - (float)hi);
-            }
-          } else {
-            const bool lower = col <= t;
-            const float dcy = __expf(lower ? sG[t] - gc : 0.f);
-            const float pv = lower ? a.scale * sRq[t] * rkc * dcy * acc[i] : 0.f;
-            const __bf16 hi = (__bf16)pv;
-            sP[t * LDT + col] = __builtin_bit_cast(uint16_t, hi);
-            sP[CT * LDT + t * LDT + col] = bf16_bits(pv - (float)hi);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int tb = 32 * mt + 8 * q4 + 4 * g;
+          const float4 G4 = *reinterpret_cast<const float4*>(sG + tb);
+          const float4 B4 = *reinterpret_cast<const float4*>(sBeta + tb);
+          const float4 K4 = *reinterpret_cast<const float4*>(sRk + tb);
+          const float4 Q4 = *reinterpret_cast<const float4*>(sRq + tb);
+          const float Gr[4] = {G4.x, G4.y, G4.z, G4.w}, Br[4] = {B4.x, B4.y, B4.z, B4.w};
+          const float Kr[4] = {K4.x, K4.y, K4.z, K4.w}, Qr[4] = {Q4.x, Q4.y, Q4.z, Q4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = tb + r;
+            const bool lower = col < t, diag_or_lower = col <= t;
+            const float dcy = __expf(diag_or_lower ? Gr[r] - gc : 0.f);
+            const float av = lower ? Br[r] * Kr[r] * rkc * dcy * gk[4 * q4 + r] : 0.f;
+            const float pv = diag_or_lower ? a.scale * Qr[r] * rkc * dcy * gq[4 * q4 + r] : 0.f;
+            if (mt == nt) sA[(32 * mt + (t - 32 * mt)) * LDA + qa * MPL + ma] = av;
+            else store_split(sT, TPL, t * LDT + col, -av);      // -A21, split operand
+            store_split(sP, TPL, t * LDT + col, pv);
           }
         }
       }
@@ -306,80 +297,93 @@ chunked_prefill_kernel(const ScanArgs a) {
     }
     __syncthreads();
 
-    // ---- 4. diagonal blocks T_bb = (I + A_bb)^-1 by forward substitution:
-    //         lane jj owns column jj % 32 of block jj / 32
-    if (wave == 0 && lane < CT) {
-      const int b = lane >> 5, cc = lane & 31;
-      const float* ab = sA + 32 * b * LDA;
-      float Tc[32];
+    // ---- 4. diagonal blocks T_bb = (I + A_bb)^-1 by forward substitution.
+    //         LPC consecutive lanes share column jj: lane part q keeps rows
+    //         q, q+LPC, ... of the column and sums their terms; a row's total
+    //         is a fixed-order lane-group sum.
+    if (tid < CT * LPC) {
+      const int jj = tid / LPC, q = tid % LPC;
+      const int b = jj >> 5, cc = jj & 31;
+      const float* ab = sA + 32 * b * LDA + q * MPL;
+      float Tl[MPL];
+#pragma unroll
+      for (int m = 0; m < MPL; ++m) Tl[m] = 0.f;
 #pragma unroll
       for (int t = 0; t < 32; ++t) {
-        float acc[4] = {t == cc ? 1.f : 0.f, 0.f, 0.f, 0.f};
+        float acc = 0.f;
+        const float* arow = ab + t * LDA;
 #pragma unroll
-        for (int i4 = 0; i4 < t; i4 += 4) {
-          const float4 av = *reinterpret_cast<const float4*>(ab + t * LDA + i4);
-          const float ar[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (i4 + u < t) acc[u] = fmaf(-ar[u], Tc[i4 + u], acc[u]);
-        }
-        Tc[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        for (int m = 0; m < (t + LPC - 1) / LPC; ++m) acc = fmaf(-arow[m], Tl[m], acc);
+        acc = group_sum<LPC>(acc) + (t == cc ? 1.f : 0.f);
+        if (q == t % LPC) Tl[t / LPC] = acc;
       }
       uint16_t* tb = sT + 32 * b * LDT + 32 * b + cc;
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
-        const __bf16 hi = (__bf16)Tc[t];
-        tb[t * LDT] = __builtin_bit_cast(uint16_t, hi);
-        tb[CT * LDT + t * LDT] = bf16_bits(Tc[t] - (float)hi);
-      }
+      for (int m = 0; m < MPL; ++m) store_split(tb, TPL, (q + LPC * m) * LDT, Tl[m]);
     }
     __syncthreads();
 
     // ---- 5. state path for this wave's 32 value columns
     {
-      // S -> split B operands
-      bf16x8 Sh[KT][2], Sl[KT][2];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        split_half<0>(S[kt], Sh[kt][0], Sl[kt][0]);
-        split_half<1>(S[kt], Sh[kt][1], Sl[kt][1]);
-      }
-      f32x16 X[NT], QS[NT];
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt) {
-        X[mt] = f32x16{};
-        QS[mt] = f32x16{};
-        const uint16_t* kr = sK + (32 * mt + c) * LDK + 4 * g;
-        const uint16_t* qr = sQ + (32 * mt + c) * LDK + 4 * g;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const bf16x8 ka = lds_a(kr + 32 * kt + 16 * h2);
-            X[mt] = mma(ka, Sh[kt][h2], X[mt]);
-            X[mt] = mma(ka, Sl[kt][h2], X[mt]);
-            const bf16x8 qa = lds_a(qr + 32 * kt + 16 * h2);
-            QS[mt] = mma(qa, Sh[kt][h2], QS[mt]);
-            QS[mt] = mma(qa, Sl[kt][h2], QS[mt]);
-          }
-      }
-      // Y = beta (V - r_k e^G X), in place of X
+      // V for this lane's rows (clamped row; rows past n are dropped below),
+      // issued first and held as packed bf16 pairs
+      uint32_t vp[NT][8];
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = 32 * mt + acc_row(i, g);
-          const float vv = t < n ? bf16_to_f32(vg[(size_t)(t0 + t) * a.v_stride + (size_t)h * DV + v]) : 0.f;
-          X[mt][i] = sBeta[t] * (vv - sCk[t] * X[mt][i]);
+        for (int i = 0; i < 16; i += 2) {
+          const int t = 32 * mt + acc_row(i, g);   // rows t and t + 1
+          const int r0 = min(t0 + t, a.n_tokens - 1), r1 = min(t0 + t + 1, a.n_tokens - 1);
+          vp[mt][i / 2] = (uint32_t)vg[(size_t)r0 * a.v_stride + v] |
+                          ((uint32_t)vg[(size_t)r1 * a.v_stride + v] << 16);
         }
-      // U1 = T11 Y1;  U2 = T22 (Y2 - A21 U1)   (3-pass split products)
-      f32x16 U[NT];
-      auto tri_mm = [&](const uint16_t* rowp, const f32x16& y, f32x16 acc) {
+      // X = K S0^T and QS = Q S0^T, S0 split per k tile on the fly
+      f32x16 X[NT], QS[NT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) { X[mt] = f32x16{}; QS[mt] = f32x16{}; }
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          bf16x8 sh, sl;
+          if (h2 == 0) split_half<0>(S[kt], sh, sl); else split_half<1>(S[kt], sh, sl);
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt) {
+            const int off = (32 * mt + c) * LDK + 4 * g + 32 * kt + 16 * h2;
+            const bf16x8 ka = lds_op(sK + off);
+            const bf16x8 qa = lds_op(sQ + off);
+            X[mt] = mma(ka, sh, X[mt]);
+            X[mt] = mma(ka, sl, X[mt]);
+            QS[mt] = mma(qa, sh, QS[mt]);
+            QS[mt] = mma(qa, sl, QS[mt]);
+          }
+        }
+      // Y = beta (V - r_k e^G X), in place of X (zero past n)
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int tb = 32 * mt + 8 * q4 + 4 * g;
+          const float4 b4 = *reinterpret_cast<const float4*>(sBeta + tb);
+          const float4 k4 = *reinterpret_cast<const float4*>(sCk + tb);
+          const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * q4 + r;
+            const uint32_t pair = vp[mt][i / 2];
+            const float vvv = bf16_to_f32((i & 1) ? (pair >> 16) : (pair & 0xFFFFu));
+            const float y = bb[r] * (vvv - kk[r] * X[mt][i]);
+            X[mt][4 * q4 + r] = tb + r < n ? y : 0.f;
+          }
+        }
+      // product of a split 32x32 LDS block (rows at rowp) with a split tile
+      auto tri_mm = [&](const uint16_t* rowp, const uint16_t* lo_plane_rowp, const f32x16& y,
+                        f32x16 acc) {
         bf16x8 yh0, yl0, yh1, yl1;
         split_half<0>(y, yh0, yl0);
         split_half<1>(y, yh1, yl1);
-        const uint16_t* lo = rowp + CT * LDT;
-        const bf16x8 a0h = lds_a(rowp), a0l = lds_a(lo), a1h = lds_a(rowp + 16), a1l = lds_a(lo + 16);
+        const bf16x8 a0h = lds_op(rowp), a0l = lds_op(lo_plane_rowp);
+        const bf16x8 a1h = lds_op(rowp + 16), a1l = lds_op(lo_plane_rowp + 16);
         acc = mma(a0h, yh0, acc);
         acc = mma(a0l, yh0, acc);
         acc = mma(a0h, yl0, acc);
@@ -388,25 +392,36 @@ chunked_prefill_kernel(const ScanArgs a) {
         acc = mma(a1h, yl1, acc);
         return acc;
       };
-      U[0] = tri_mm(sT + c * LDT + 4 * g, X[0], f32x16{});
-      if constexpr (NT == 2) {
-        const f32x16 w = tri_mm(sT + (32 + c) * LDT + 4 * g, U[0], X[1]);        // Y2 - A21 U1
-        U[1] = tri_mm(sT + (32 + c) * LDT + 32 + 4 * g, w, f32x16{});
+      // U1 = T11 Y1;  U2 = T22 (Y2 - A21 U1)
+      f32x16 U[NT];
+      {
+        const uint16_t* r0 = sT + c * LDT + 4 * g;
+        U[0] = tri_mm(r0, r0 + TPL, X[0], f32x16{});
+        if constexpr (NT == 2) {
+          const uint16_t* r1 = sT + (32 + c) * LDT + 4 * g;
+          const f32x16 w = tri_mm(r1, r1 + TPL, U[0], X[1]);
+          U[1] = tri_mm(r1 + 32, r1 + 32 + TPL, w, f32x16{});
+        }
       }
-      // O = scale r_q e^G (Q S0^T) + P U, written for the chunk's valid rows
+      // O = scale r_q e^G (Q S0^T) + P U -> out rows < n
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) QS[mt][i] *= sCq[32 * mt + acc_row(i, g)];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 c4 = *reinterpret_cast<const float4*>(sCq + 32 * mt + 8 * q4 + 4 * g);
+          QS[mt][4 * q4] *= c4.x; QS[mt][4 * q4 + 1] *= c4.y;
+          QS[mt][4 * q4 + 2] *= c4.z; QS[mt][4 * q4 + 3] *= c4.w;
+        }
+        const uint16_t* pr = sP + (32 * mt + c) * LDT + 4 * g;
 #pragma unroll
-        for (int m2 = 0; m2 <= mt; ++m2) QS[mt] = tri_mm(sP + (32 * mt + c) * LDT + 32 * m2 + 4 * g, U[m2], QS[mt]);
+        for (int m2 = 0; m2 <= mt; ++m2) QS[mt] = tri_mm(pr + 32 * m2, pr + 32 * m2 + TPL, U[m2], QS[mt]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int t = 32 * mt + acc_row(i, g);
-          if (t < n) og[((size_t)(t0 + t) * a.Hv + h) * DV + v] = bf16_bits(QS[mt][i]);
+          if (t < n) og[(size_t)(t0 + t) * a.Hv * DV + v] = bf16_bits(QS[mt][i]);
         }
       }
-      // S = e^{G_C} S + K^T (r_k e^{G_C - G} U)
+      // S = e^{G_C} S + K^T (r_k e^{G_C - G} U); K^T operand gathered from K rows
       const float gC = __expf(sG[CT - 1]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
@@ -415,19 +430,30 @@ chunked_prefill_kernel(const ScanArgs a) {
 #pragma unroll
       for (int m2 = 0; m2 < NT; ++m2) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) U[m2][i] *= sCu[32 * m2 + acc_row(i, g)];
-        bf16x8 uh0, ul0, uh1, ul1;
-        split_half<0>(U[m2], uh0, ul0);
-        split_half<1>(U[m2], uh1, ul1);
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          const uint16_t* kr = sKT + (32 * kt + c) * LDT + 32 * m2 + 4 * g;
-          const bf16x8 a0 = lds_a(kr), a1 = lds_a(kr + 16);
-          S[kt] = mma(a0, uh0, S[kt]);
-          S[kt] = mma(a0, ul0, S[kt]);
-          S[kt] = mma(a1, uh1, S[kt]);
-          S[kt] = mma(a1, ul1, S[kt]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 c4 = *reinterpret_cast<const float4*>(sCu + 32 * m2 + 8 * q4 + 4 * g);
+          U[m2][4 * q4] *= c4.x; U[m2][4 * q4 + 1] *= c4.y;
+          U[m2][4 * q4 + 2] *= c4.z; U[m2][4 * q4 + 3] *= c4.w;
         }
+        bf16x8 uh[2], ul[2];
+        split_half<0>(U[m2], uh[0], ul[0]);
+        split_half<1>(U[m2], uh[1], ul[1]);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            // A operand: rows k = 32kt + c, k-order (tokens) 32*m2 + 16*h2 + 4g + {0..3, 8..11}
+            const uint16_t* kc = sK + (32 * m2 + 16 * h2 + 4 * g) * LDK + 32 * kt + c;
+            uint32_t w[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const int r = (p < 2 ? 0 : 8) + 2 * (p & 1);
+              w[p] = (uint32_t)kc[r * LDK] | ((uint32_t)kc[(r + 1) * LDK] << 16);
+            }
+            const bf16x8 ka = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+            S[kt] = mma(ka, uh[h2], S[kt]);
+            S[kt] = mma(ka, ul[h2], S[kt]);
+          }
       }
     }
     if (t0 + n == next_ck) {
@@ -457,9 +483,14 @@ chunked_prefill_kernel(const ScanArgs a) {
     hipLaunchKernelGGL(kern, dim3(a.n_seqs, a.Hv), dim3(C::NTH), C::bytes, st, a);         \
     return hipGetLastError();                                                              \
   }                                                                                        \
+  /* The scan runs 32-token chunks for chunk = 32 or 64 (a 64-grid checkpoint  */         \
+  /* is on the 32-grid too) and 16-token chunks, zero-padded, for chunk = 16:  */         \
+  /* the 64-row tile needs more than the 256 registers of two workgroups/CU.   */         \
   template <int DV>                                                                        \
   static hipError_t launch_nt(const ScanArgs& a, hipStream_t st) {                         \
-    return a.chunk > 32 ? launch_one<DV, 2>(a, st) : launch_one<DV, 1>(a, st);             \
+    ScanArgs b = a;                                                                        \
+    b.chunk = a.chunk > 32 ? 32 : a.chunk;                                                 \
+    return launch_one<DV, 1>(b, st);                                                       \
   }                                                                                        \
   hipError_t launch_dk##DKV(const ScanArgs& a, hipStream_t st) {                           \
     if (a.dv == 32) return launch_nt<32>(a, st);                                           \
