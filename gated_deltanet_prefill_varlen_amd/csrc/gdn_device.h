@@ -91,12 +91,24 @@ __device__ __forceinline__ void store16f(float* p, const float* v) {
 }
 
 // ------------------------------------------------------- lane reductions --
-// Sum over aligned groups of W consecutive lanes (W a power of two <= 64);
-// every lane of the group receives the same total, summed in a fixed order.
+// Lane exchange inside a row of 16 lanes (DPP, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 16):
+// pairs, then quads (quad_perm), then the two quads of a half-row
+// (row_half_mirror), then the two halves of a row (row_mirror).  Each step
+// adds a value equal on both partners, so every lane of the group ends with
+// the same bits.
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) x += __shfl_xor(x, m, 64);
+  static_assert(W >= 1 && W <= 16 && (W & (W - 1)) == 0, "group width");
+  if constexpr (W >= 2) x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) x += dpp_f32<0x141>(x);  // row_half_mirror
+  if constexpr (W >= 16) x += dpp_f32<0x140>(x); // row_mirror
   return x;
 }
 

@@ -104,7 +104,9 @@ struct Cfg {
   static constexpr int LDA = 32 + 4;      // row stride of a diagonal block of A (fp32)
   static constexpr int oK = 0;
   static constexpr int oQ = oK + CT * LDK * 2;
-  static constexpr int oT = oQ + CT * LDK * 2;        // hi then lo plane: T11, -A21, T22
+  static constexpr int LDV = DV + 8;      // row stride of the V / O tile (bf16; 16-byte rows)
+  static constexpr int oV = oQ + CT * LDK * 2;        // V tile, then the O tile
+  static constexpr int oT = oV + CT * LDV * 2;        // hi then lo plane: T11, -A21, T22
   static constexpr int oP = oT + 2 * CT * LDT * 2;    // hi then lo plane
   static constexpr int oA = oP + 2 * CT * LDT * 2;    // NT diagonal blocks of A, lane-interleaved
   static constexpr int oS = oA + NT * 32 * LDA * 4;   // per-token scalars
@@ -122,10 +124,11 @@ __global__ void __launch_bounds__(64 * (DV / 32), 2)
 chunked_prefill_kernel(const ScanArgs a) {
   using C = Cfg<DK, DV, NT>;
   constexpr int CT = C::CT, NTH = C::NTH, KT = C::KT, LDK = C::LDK, LDT = C::LDT, LDA = C::LDA;
-  constexpr int LPC = C::LPC, MPL = C::MPL;
+  constexpr int LPC = C::LPC, MPL = C::MPL, LDV = C::LDV;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* sK = reinterpret_cast<uint16_t*>(smem + C::oK);
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + C::oQ);
+  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + C::oV);
   uint16_t* sT = reinterpret_cast<uint16_t*>(smem + C::oT);
   uint16_t* sP = reinterpret_cast<uint16_t*>(smem + C::oP);
   float* sA = reinterpret_cast<float*>(smem + C::oA);
@@ -178,6 +181,7 @@ chunked_prefill_kernel(const ScanArgs a) {
   int ci = lower_bound_i32(a.ckpt, a.n_ckpt, seq0 + 1);
   int next_ck = ci < a.n_ckpt ? a.ckpt[ci] : INT_MAX;
 
+  int pt0 = 0, pn = 0;   // previous chunk: its O tile is still in the V/O LDS tile
   for (int t0 = seq0; t0 < seq1; t0 += a.chunk) {
     const int n = min(a.chunk, seq1 - t0);   // valid rows of this chunk
 
@@ -193,6 +197,16 @@ chunked_prefill_kernel(const ScanArgs a) {
       u32x2* qd = reinterpret_cast<u32x2*>(sQ + t * LDK + c8);
       kd[0] = u32x2{kv.x, kv.y}; kd[1] = u32x2{kv.z, kv.w};
       qd[0] = u32x2{qv.x, qv.y}; qd[1] = u32x2{qv.z, qv.w};
+    }
+    // previous chunk's O rows out (16-byte stores), then this chunk's V rows
+    // in; a thread owns the same 16-byte segments for both, so no race
+    for (int e = tid; e < CT * DV / 8; e += NTH) {
+      const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+      u32x4* seg = reinterpret_cast<u32x4*>(sV + t * LDV + c8);
+      if (t < pn) *reinterpret_cast<u32x4*>(og + (size_t)(pt0 + t) * a.Hv * DV + c8) = *seg;
+      u32x4 vv = {0u, 0u, 0u, 0u};
+      if (t < n) vv = *reinterpret_cast<const u32x4*>(vg + (size_t)(t0 + t) * a.v_stride + c8);
+      *seg = vv;
     }
     if (tid < CT) {
       const bool ok = tid < n;
@@ -251,40 +265,37 @@ chunked_prefill_kernel(const ScanArgs a) {
     // ---- 3. Gram and Q K^T tiles (MFMA, shared K operand) -> A, P; scalars
     {
       constexpr int NTILE = NT * (NT + 1) / 2;
-      for (int tix = wave; tix < NTILE; tix += C::NW) {
+      for (int job = wave; job < 2 * NTILE; job += C::NW) {
+        const bool gram = job < NTILE;                 // Gram K K^T, else Q K^T
+        const int tix = gram ? job : job - NTILE;
         const int mt = tix == 0 ? 0 : 1, nt = tix == 2 ? 1 : 0;
-        const uint16_t* kr = sK + (32 * mt + c) * LDK + 4 * g;
-        const uint16_t* qr = sQ + (32 * mt + c) * LDK + 4 * g;
+        const uint16_t* ar = (gram ? sK : sQ) + (32 * mt + c) * LDK + 4 * g;
         const uint16_t* br = sK + (32 * nt + c) * LDK + 4 * g;
-        f32x16 gk = {}, gq = {};
+        f32x16 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < DK / 16; ++ks) {
-          const bf16x8 b = lds_op(br + 16 * ks);
-          gk = mma(lds_op(kr + 16 * ks), b, gk);
-          gq = mma(lds_op(qr + 16 * ks), b, gq);
-        }
+        for (int ks = 0; ks < DK / 16; ++ks) acc = mma(lds_op(ar + 16 * ks), lds_op(br + 16 * ks), acc);
         const int col = 32 * nt + c, lcol = c;   // global / block-local column
         const float gc = sG[col], rkc = sRk[col];
         const int qa = lcol % LPC, ma = lcol / LPC;
+        const float* rowsc = gram ? sRk : sRq;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int tb = 32 * mt + 8 * q4 + 4 * g;
           const float4 G4 = *reinterpret_cast<const float4*>(sG + tb);
           const float4 B4 = *reinterpret_cast<const float4*>(sBeta + tb);
-          const float4 K4 = *reinterpret_cast<const float4*>(sRk + tb);
-          const float4 Q4 = *reinterpret_cast<const float4*>(sRq + tb);
+          const float4 R4 = *reinterpret_cast<const float4*>(rowsc + tb);
           const float Gr[4] = {G4.x, G4.y, G4.z, G4.w}, Br[4] = {B4.x, B4.y, B4.z, B4.w};
-          const float Kr[4] = {K4.x, K4.y, K4.z, K4.w}, Qr[4] = {Q4.x, Q4.y, Q4.z, Q4.w};
+          const float Rr[4] = {R4.x, R4.y, R4.z, R4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = tb + r;
-            const bool lower = col < t, diag_or_lower = col <= t;
-            const float dcy = __expf(diag_or_lower ? Gr[r] - gc : 0.f);
-            const float av = lower ? Br[r] * Kr[r] * rkc * dcy * gk[4 * q4 + r] : 0.f;
-            const float pv = diag_or_lower ? a.scale * Qr[r] * rkc * dcy * gq[4 * q4 + r] : 0.f;
-            if (mt == nt) sA[(32 * mt + (t - 32 * mt)) * LDA + qa * MPL + ma] = av;
-            else store_split(sT, TPL, t * LDT + col, -av);      // -A21, split operand
-            store_split(sP, TPL, t * LDT + col, pv);
+            const bool on = gram ? col < t : col <= t;
+            const float dcy = __expf(on ? Gr[r] - gc : 0.f);
+            const float f = (gram ? Br[r] : a.scale) * Rr[r] * rkc * dcy * acc[4 * q4 + r];
+            const float val = on ? f : 0.f;
+            if (!gram) store_split(sP, TPL, t * LDT + col, val);
+            else if (mt == nt) sA[t * LDA + qa * MPL + ma] = val;
+            else store_split(sT, TPL, t * LDT + col, -val);      // -A21, split operand
           }
         }
       }
@@ -310,12 +321,15 @@ chunked_prefill_kernel(const ScanArgs a) {
       for (int m = 0; m < MPL; ++m) Tl[m] = 0.f;
 #pragma unroll
       for (int t = 0; t < 32; ++t) {
-        float acc = 0.f;
+        float acc0 = 0.f, acc1 = 0.f;
         const float* arow = ab + t * LDA;
 #pragma unroll
-        for (int m = 0; m < (t + LPC - 1) / LPC; ++m) acc = fmaf(-arow[m], Tl[m], acc);
-        acc = group_sum<LPC>(acc) + (t == cc ? 1.f : 0.f);
-        if (q == t % LPC) Tl[t / LPC] = acc;
+        for (int m = 0; m < (t + LPC - 1) / LPC; ++m) {
+          if (m & 1) acc1 = fmaf(-arow[m], Tl[m], acc1);
+          else acc0 = fmaf(-arow[m], Tl[m], acc0);
+        }
+        const float tot = group_sum<LPC>(acc0 + acc1) + (t == cc ? 1.f : 0.f);
+        if (q == t % LPC) Tl[t / LPC] = tot;
       }
       uint16_t* tb = sT + 32 * b * LDT + 32 * b + cc;
 #pragma unroll
@@ -325,18 +339,6 @@ chunked_prefill_kernel(const ScanArgs a) {
 
     // ---- 5. state path for this wave's 32 value columns
     {
-      // V for this lane's rows (clamped row; rows past n are dropped below),
-      // issued first and held as packed bf16 pairs
-      uint32_t vp[NT][8];
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const int t = 32 * mt + acc_row(i, g);   // rows t and t + 1
-          const int r0 = min(t0 + t, a.n_tokens - 1), r1 = min(t0 + t + 1, a.n_tokens - 1);
-          vp[mt][i / 2] = (uint32_t)vg[(size_t)r0 * a.v_stride + v] |
-                          ((uint32_t)vg[(size_t)r1 * a.v_stride + v] << 16);
-        }
       // X = K S0^T and QS = Q S0^T, S0 split per k tile on the fly
       f32x16 X[NT], QS[NT];
 #pragma unroll
@@ -370,8 +372,7 @@ chunked_prefill_kernel(const ScanArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * q4 + r;
-            const uint32_t pair = vp[mt][i / 2];
-            const float vvv = bf16_to_f32((i & 1) ? (pair >> 16) : (pair & 0xFFFFu));
+            const float vvv = bf16_to_f32(sV[(tb + r) * LDV + v]);
             const float y = bb[r] * (vvv - kk[r] * X[mt][i]);
             X[mt][4 * q4 + r] = tb + r < n ? y : 0.f;
           }
@@ -415,11 +416,10 @@ chunked_prefill_kernel(const ScanArgs a) {
         const uint16_t* pr = sP + (32 * mt + c) * LDT + 4 * g;
 #pragma unroll
         for (int m2 = 0; m2 <= mt; ++m2) QS[mt] = tri_mm(pr + 32 * m2, pr + 32 * m2 + TPL, U[m2], QS[mt]);
+        // O into this wave's own columns of the V/O tile (V of these columns
+        // was consumed above by this wave only); stored out next chunk
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = 32 * mt + acc_row(i, g);
-          if (t < n) og[(size_t)(t0 + t) * a.Hv * DV + v] = bf16_bits(QS[mt][i]);
-        }
+        for (int i = 0; i < 16; ++i) sV[(32 * mt + acc_row(i, g)) * LDV + v] = bf16_bits(QS[mt][i]);
       }
       // S = e^{G_C} S + K^T (r_k e^{G_C - G} U); K^T operand gathered from K rows
       const float gC = __expf(sG[CT - 1]);
@@ -461,7 +461,15 @@ chunked_prefill_kernel(const ScanArgs a) {
       ++ci;
       next_ck = ci < a.n_ckpt ? a.ckpt[ci] : INT_MAX;
     }
+    pt0 = t0;
+    pn = n;
     __syncthreads();
+  }
+  for (int e = tid; e < CT * DV / 8; e += NTH) {   // last chunk's O rows
+    const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+    if (t < pn)
+      *reinterpret_cast<u32x4*>(og + (size_t)(pt0 + t) * a.Hv * DV + c8) =
+          *reinterpret_cast<const u32x4*>(sV + t * LDV + c8);
   }
   if (a.final_state) store_state(a.final_state + (size_t)s * sstride + ((size_t)h * DV + v) * DK);
 }
