@@ -65,17 +65,39 @@ __device__ __forceinline__ bf16x8 lds_op(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as packed bf16 hi terms and packed bf16 lo terms
+// (hi = bf16(x), lo = bf16(x - hi)), two values per conversion.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xFFFF0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
+}
+
 // Accumulator half h2 (registers 8h2..8h2+7) as a B operand, split into
 // hi + lo bf16 terms.
 template <int H2>
 __device__ __forceinline__ void split_half(const f32x16& x, bf16x8& hi, bf16x8& lo) {
+  uint32_t hw[4], lw[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float f = x[8 * H2 + j];
-    const __bf16 h = (__bf16)f;
-    hi[j] = h;
-    lo[j] = (__bf16)(f - (float)h);
+  for (int p = 0; p < 4; ++p) split2(x[8 * H2 + 2 * p], x[8 * H2 + 2 * p + 1], hw[p], lw[p]);
+  hi = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+}
+
+// Sum of squares of the eight bf16 values in a 16-byte vector.
+__device__ __forceinline__ float sumsq8(const u32x4& w) {
+  float s = 0.f;
+  const uint32_t r[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float x0 = __uint_as_float(r[p] << 16), x1 = __uint_as_float(r[p] & 0xFFFF0000u);
+    s = fmaf(x0, x0, s);
+    s = fmaf(x1, x1, s);
   }
+  return s;
 }
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
@@ -99,7 +121,7 @@ struct Cfg {
   static constexpr int LDT = CT + 4;      // row stride of sT, sP (bf16)
   // forward substitution: LPC lanes per column of the diagonal blocks
   static constexpr int LPC_RAW = NTH / CT;
-  static constexpr int LPC = LPC_RAW > 8 ? 8 : (LPC_RAW < 1 ? 1 : LPC_RAW);
+  static constexpr int LPC = LPC_RAW > 4 ? 4 : (LPC_RAW < 1 ? 1 : LPC_RAW);
   static constexpr int MPL = 32 / LPC;    // rows of a column held per lane
   static constexpr int LDA = 32 + 4;      // row stride of a diagonal block of A (fp32)
   static constexpr int oK = 0;
@@ -185,18 +207,32 @@ chunked_prefill_kernel(const ScanArgs a) {
   for (int t0 = seq0; t0 < seq1; t0 += a.chunk) {
     const int n = min(a.chunk, seq1 - t0);   // valid rows of this chunk
 
-    // ---- 1. stage K, Q rows (zero past n), log-gates and betas
-    for (int e = tid; e < CT * DK / 8; e += NTH) {
-      const int t = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-      u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-      if (t < n) {
-        kv = *reinterpret_cast<const u32x4*>(kg + (size_t)(t0 + t) * a.k_stride + (size_t)j * DK + c8);
-        qv = *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + t) * a.q_stride + (size_t)j * DK + c8);
+    // ---- 1. stage K, Q rows (zero past n) with their L2 norms (squares summed
+    //         in registers, then over the row's lanes), V rows (after the
+    //         previous chunk's O rows leave), betas and the gate cumsum
+    {
+      constexpr int VPR = DK / 8;          // 16-byte vectors per row = lanes per row
+      static_assert((CT * DK / 8) % 64 == 0 && VPR <= 16, "row lanes");
+      for (int e = tid; e < CT * DK / 8; e += NTH) {   // whole waves per trip
+        const int t = e / VPR, c8 = (e % VPR) * 8;
+        u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+        if (t < n) {
+          kv = *reinterpret_cast<const u32x4*>(kg + (size_t)(t0 + t) * a.k_stride + (size_t)j * DK + c8);
+          qv = *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + t) * a.q_stride + (size_t)j * DK + c8);
+        }
+        u32x2* kd = reinterpret_cast<u32x2*>(sK + t * LDK + c8);
+        u32x2* qd = reinterpret_cast<u32x2*>(sQ + t * LDK + c8);
+        kd[0] = u32x2{kv.x, kv.y}; kd[1] = u32x2{kv.z, kv.w};
+        qd[0] = u32x2{qv.x, qv.y}; qd[1] = u32x2{qv.z, qv.w};
+        float sk = sumsq8(kv), sq = sumsq8(qv);
+        sk = group_sum<VPR>(sk);
+        sq = group_sum<VPR>(sq);
+        if (e % VPR == 0) {   // zero-padded rows past n keep r = 1 (no 0 * inf)
+          const bool nrm = a.l2norm && t < n;
+          sRk[t] = nrm ? 1.0f / sqrtf(sk + a.eps) : 1.0f;
+          sRq[t] = nrm ? 1.0f / sqrtf(sq + a.eps) : 1.0f;
+        }
       }
-      u32x2* kd = reinterpret_cast<u32x2*>(sK + t * LDK + c8);
-      u32x2* qd = reinterpret_cast<u32x2*>(sQ + t * LDK + c8);
-      kd[0] = u32x2{kv.x, kv.y}; kd[1] = u32x2{kv.z, kv.w};
-      qd[0] = u32x2{qv.x, qv.y}; qd[1] = u32x2{qv.z, qv.w};
     }
     // previous chunk's O rows out (16-byte stores), then this chunk's V rows
     // in; a thread owns the same 16-byte segments for both, so no race
@@ -208,57 +244,21 @@ chunked_prefill_kernel(const ScanArgs a) {
       if (t < n) vv = *reinterpret_cast<const u32x4*>(vg + (size_t)(t0 + t) * a.v_stride + c8);
       *seg = vv;
     }
-    if (tid < CT) {
-      const bool ok = tid < n;
-      sG[tid] = ok ? a.g[(size_t)(t0 + tid) * a.Hv + h] : 0.f;
-      sBeta[tid] = ok ? a.beta[(size_t)(t0 + tid) * a.Hv + h] : 0.f;
-    }
-    __syncthreads();
-
-    // ---- 2. row norms, gate cumsum
-    {
-      constexpr int TPR_RAW = NTH / CT >= 1 ? NTH / CT : 1;   // lanes per row
-      constexpr int TPR = TPR_RAW < DK / 8 ? TPR_RAW : DK / 8;
-      constexpr int PER = DK / TPR;
-      constexpr int RPP = NTH / TPR;  // rows per pass
-      static_assert(PER % 8 == 0 && (TPR & (TPR - 1)) == 0, "norm split");
-      for (int r0 = 0; r0 < CT; r0 += RPP) {
-        const int t = r0 + tid / TPR;
-        const bool valid = t < CT;   // RPP may exceed CT; those lanes compute row 0 and discard
-        const int tt = valid ? t : 0;
-        const int part = tid % TPR;
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int e = 0; e < PER; e += 4) {
-          const int col = part * PER + e;
-          const u32x2 kk = *reinterpret_cast<const u32x2*>(sK + tt * LDK + col);
-          const u32x2 qq = *reinterpret_cast<const u32x2*>(sQ + tt * LDK + col);
-          const uint32_t kw[2] = {kk.x, kk.y}, qw[2] = {qq.x, qq.y};
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const float k0 = bf16_to_f32(kw[p] & 0xFFFFu), k1 = bf16_to_f32(kw[p] >> 16);
-            const float q0 = bf16_to_f32(qw[p] & 0xFFFFu), q1 = bf16_to_f32(qw[p] >> 16);
-            sk = fmaf(k0, k0, sk); sk = fmaf(k1, k1, sk);
-            sq = fmaf(q0, q0, sq); sq = fmaf(q1, q1, sq);
-          }
-        }
-        sk = group_sum<TPR>(sk);
-        sq = group_sum<TPR>(sq);
-        if (valid && part == 0) {   // zero-padded rows past n keep r = 1 (no 0 * inf)
-          const bool nrm = a.l2norm && t < n;
-          sRk[t] = nrm ? 1.0f / sqrtf(sk + a.eps) : 1.0f;
-          sRq[t] = nrm ? 1.0f / sqrtf(sq + a.eps) : 1.0f;
-        }
+    if (wave == 0) {  // betas and the inclusive scan of the log-gates (fixed order)
+      float x = 0.f, b = 0.f;
+      if (lane < n) {
+        x = a.g[(size_t)(t0 + lane) * a.Hv + h];
+        b = a.beta[(size_t)(t0 + lane) * a.Hv + h];
       }
-    }
-    if (wave == 0) {  // inclusive scan of the log-gates over the chunk (fixed order)
-      float x = lane < CT ? sG[lane] : 0.f;
 #pragma unroll
       for (int d = 1; d < CT; d <<= 1) {
         const float y = __shfl_up(x, d, 64);
         if (lane >= d) x += y;
       }
-      if (lane < CT) sG[lane] = x;
+      if (lane < CT) {
+        sG[lane] = x;
+        sBeta[lane] = b;
+      }
     }
     __syncthreads();
 
