@@ -136,6 +136,11 @@ struct Cfg {
   static constexpr int bytes = oS + kScal * CT * 4;
   static_assert(bytes <= 80 * 1024, "two workgroups per CU");
   static_assert(LPC * CT <= NTH || LPC == 1, "substitution lanes");
+  // the next chunk's rows wait in registers (16-byte vectors per thread)
+  // while this chunk computes, when they fit in 32 registers
+  static constexpr int NVK = (CT * DK / 8 + NTH - 1) / NTH;
+  static constexpr int NVV = (CT * DV / 8 + NTH - 1) / NTH;
+  static constexpr bool PREFETCH = (2 * NVK + NVV) * 4 <= 32;
 };
 
 // per-token scalar arrays (index into the scalar block)
@@ -200,67 +205,115 @@ chunked_prefill_kernel(const ScanArgs a) {
             make_float4(S[kt][4 * q4], S[kt][4 * q4 + 1], S[kt][4 * q4 + 2], S[kt][4 * q4 + 3]);
   };
 
-  int ci = lower_bound_i32(a.ckpt, a.n_ckpt, seq0 + 1);
-  int next_ck = ci < a.n_ckpt ? a.ckpt[ci] : INT_MAX;
+  // checkpoint cursor, uniform over the workgroup; the positions are read
+  // through the constant address space so they come in by scalar loads and
+  // never wait behind the vector loads in flight
+  typedef const int32_t __attribute__((address_space(4)))* ConstI32;
+  const ConstI32 ckp = (ConstI32)a.ckpt;
+  int ci = __builtin_amdgcn_readfirstlane(lower_bound_i32(a.ckpt, a.n_ckpt, seq0 + 1));
+  int next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
+
+  // One chunk's HBM rows into registers.  Every lane loads (row index clamped
+  // into the chunk, so no load is conditional); rows past the chunk's end are
+  // zeroed where they are consumed.
+  u32x4 pk[C::NVK], pq[C::NVK], pv[C::NVV];
+  float pg, pb;
+  auto fetch = [&](int t0x, int nx) {
+#pragma unroll
+    for (int u = 0; u < C::NVK; ++u) {
+      const int e = min(tid + u * NTH, CT * DK / 8 - 1);
+      const int t = min(e / (DK / 8), nx - 1), c8 = (e % (DK / 8)) * 8;
+      pk[u] = *reinterpret_cast<const u32x4*>(kg + (size_t)(t0x + t) * a.k_stride + (size_t)j * DK + c8);
+      pq[u] = *reinterpret_cast<const u32x4*>(qg + (size_t)(t0x + t) * a.q_stride + (size_t)j * DK + c8);
+    }
+#pragma unroll
+    for (int u = 0; u < C::NVV; ++u) {
+      const int e = min(tid + u * NTH, CT * DV / 8 - 1);
+      const int t = min(e / (DV / 8), nx - 1), c8 = (e % (DV / 8)) * 8;
+      pv[u] = *reinterpret_cast<const u32x4*>(vg + (size_t)(t0x + t) * a.v_stride + c8);
+    }
+    const int tl = min(lane, nx - 1);
+    pg = a.g[(size_t)(t0x + tl) * a.Hv + h];
+    pb = a.beta[(size_t)(t0x + tl) * a.Hv + h];
+  };
+  if constexpr (C::PREFETCH)
+    if (seq1 > seq0) fetch(seq0, min(a.chunk, seq1 - seq0));
+  // drain the state and first-chunk loads here, so that no wait inside the
+  // chunk loop has to cover them (vmcnt(0); expcnt, lgkmcnt unchanged)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   int pt0 = 0, pn = 0;   // previous chunk: its O tile is still in the V/O LDS tile
   for (int t0 = seq0; t0 < seq1; t0 += a.chunk) {
     const int n = min(a.chunk, seq1 - t0);   // valid rows of this chunk
 
     // ---- 1. stage K, Q rows (zero past n) with their L2 norms (squares summed
-    //         in registers, then over the row's lanes), V rows (after the
-    //         previous chunk's O rows leave), betas and the gate cumsum
+    //         in registers, then over the row's lanes), V rows, betas and the
+    //         gate cumsum.  The rows were fetched into registers while the
+    //         previous chunk ran.  The previous chunk's O rows leave the V/O
+    //         tile first: read into registers before V lands, stored to HBM
+    //         after (global stores issued after the loads are consumed).
+    if constexpr (!C::PREFETCH) fetch(t0, n);
     {
       constexpr int VPR = DK / 8;          // 16-byte vectors per row = lanes per row
       static_assert((CT * DK / 8) % 64 == 0 && VPR <= 16, "row lanes");
-      for (int e = tid; e < CT * DK / 8; e += NTH) {   // whole waves per trip
-        const int t = e / VPR, c8 = (e % VPR) * 8;
-        u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-        if (t < n) {
-          kv = *reinterpret_cast<const u32x4*>(kg + (size_t)(t0 + t) * a.k_stride + (size_t)j * DK + c8);
-          qv = *reinterpret_cast<const u32x4*>(qg + (size_t)(t0 + t) * a.q_stride + (size_t)j * DK + c8);
-        }
-        u32x2* kd = reinterpret_cast<u32x2*>(sK + t * LDK + c8);
-        u32x2* qd = reinterpret_cast<u32x2*>(sQ + t * LDK + c8);
-        kd[0] = u32x2{kv.x, kv.y}; kd[1] = u32x2{kv.z, kv.w};
-        qd[0] = u32x2{qv.x, qv.y}; qd[1] = u32x2{qv.z, qv.w};
-        float sk = sumsq8(kv), sq = sumsq8(qv);
-        sk = group_sum<VPR>(sk);
-        sq = group_sum<VPR>(sq);
-        if (e % VPR == 0) {   // zero-padded rows past n keep r = 1 (no 0 * inf)
-          const bool nrm = a.l2norm && t < n;
-          sRk[t] = nrm ? 1.0f / sqrtf(sk + a.eps) : 1.0f;
-          sRq[t] = nrm ? 1.0f / sqrtf(sq + a.eps) : 1.0f;
+#pragma unroll
+      for (int u = 0; u < C::NVK; ++u) {
+        const int e = tid + u * NTH;
+        if (e < CT * DK / 8) {             // whole waves per trip
+          const int t = e / VPR, c8 = (e % VPR) * 8;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 kv = t < n ? pk[u] : z, qv = t < n ? pq[u] : z;
+          u32x2* kd = reinterpret_cast<u32x2*>(sK + t * LDK + c8);
+          u32x2* qd = reinterpret_cast<u32x2*>(sQ + t * LDK + c8);
+          kd[0] = u32x2{kv.x, kv.y}; kd[1] = u32x2{kv.z, kv.w};
+          qd[0] = u32x2{qv.x, qv.y}; qd[1] = u32x2{qv.z, qv.w};
+          float sk = sumsq8(kv), sq = sumsq8(qv);
+          sk = group_sum<VPR>(sk);
+          sq = group_sum<VPR>(sq);
+          if (e % VPR == 0) {   // zero-padded rows past n keep r = 1 (no 0 * inf)
+            const bool nrm = a.l2norm && t < n;
+            sRk[t] = nrm ? 1.0f / sqrtf(sk + a.eps) : 1.0f;
+            sRq[t] = nrm ? 1.0f / sqrtf(sq + a.eps) : 1.0f;
+          }
         }
       }
     }
-    // previous chunk's O rows out (16-byte stores), then this chunk's V rows
-    // in; a thread owns the same 16-byte segments for both, so no race
-    for (int e = tid; e < CT * DV / 8; e += NTH) {
-      const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-      u32x4* seg = reinterpret_cast<u32x4*>(sV + t * LDV + c8);
-      if (t < pn) *reinterpret_cast<u32x4*>(og + (size_t)(pt0 + t) * a.Hv * DV + c8) = *seg;
-      u32x4 vv = {0u, 0u, 0u, 0u};
-      if (t < n) vv = *reinterpret_cast<const u32x4*>(vg + (size_t)(t0 + t) * a.v_stride + c8);
-      *seg = vv;
-    }
-    if (wave == 0) {  // betas and the inclusive scan of the log-gates (fixed order)
-      float x = 0.f, b = 0.f;
-      if (lane < n) {
-        x = a.g[(size_t)(t0 + lane) * a.Hv + h];
-        b = a.beta[(size_t)(t0 + lane) * a.Hv + h];
+    {
+      // a thread owns the same 16-byte segments of the V/O tile for both
+      u32x4 ov[C::NVV];
+#pragma unroll
+      for (int u = 0; u < C::NVV; ++u) {
+        const int e = tid + u * NTH;
+        if (e < CT * DV / 8) {
+          const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+          u32x4* seg = reinterpret_cast<u32x4*>(sV + t * LDV + c8);
+          ov[u] = *seg;
+          *seg = t < n ? pv[u] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      if (wave == 0) {  // betas and the inclusive scan of the log-gates (fixed order)
+        float x = lane < n ? pg : 0.f;
+#pragma unroll
+        for (int d = 1; d < CT; d <<= 1) {
+          const float y = __shfl_up(x, d, 64);
+          if (lane >= d) x += y;
+        }
+        if (lane < CT) {
+          sG[lane] = x;
+          sBeta[lane] = lane < n ? pb : 0.f;
+        }
       }
 #pragma unroll
-      for (int d = 1; d < CT; d <<= 1) {
-        const float y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-      }
-      if (lane < CT) {
-        sG[lane] = x;
-        sBeta[lane] = b;
+      for (int u = 0; u < C::NVV; ++u) {
+        const int e = tid + u * NTH;
+        const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+        if (e < CT * DV / 8 && t < pn)
+          *reinterpret_cast<u32x4*>(og + (size_t)(pt0 + t) * a.Hv * DV + c8) = ov[u];
       }
     }
     __syncthreads();
+    if constexpr (C::PREFETCH)
+      if (t0 + a.chunk < seq1) fetch(t0 + a.chunk, min(a.chunk, seq1 - t0 - a.chunk));
 
     // ---- 3. Gram and Q K^T tiles (MFMA, shared K operand) -> A, P; scalars
     {
@@ -458,8 +511,8 @@ chunked_prefill_kernel(const ScanArgs a) {
     }
     if (t0 + n == next_ck) {
       store_state(a.ckpt_buf + (size_t)ci * sstride + ((size_t)h * DV + v) * DK);
-      ++ci;
-      next_ck = ci < a.n_ckpt ? a.ckpt[ci] : INT_MAX;
+      ci = __builtin_amdgcn_readfirstlane(ci + 1);
+      next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
     }
     pt0 = t0;
     pn = n;
