@@ -33,6 +33,7 @@
 #pragma once
 
 #include <climits>
+#include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -100,6 +101,33 @@ __device__ __forceinline__ float sumsq8(const u32x4& w) {
   return s;
 }
 
+// Inclusive prefix sum over lanes 0..31 (each 16-lane row by shifts of 1, 2,
+// 4, 8, then row 0's total into row 1); a fixed order on every call.
+__device__ __forceinline__ float scan32(float x) {
+  auto shr = [](float v, auto ctrl) {   // lanes shifted in from outside the row read 0
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 decltype(ctrl)::value, 0xF, 0xF, true));
+  };
+  x += shr(x, std::integral_constant<int, 0x111>{});   // row_shr:1
+  x += shr(x, std::integral_constant<int, 0x112>{});   // row_shr:2
+  x += shr(x, std::integral_constant<int, 0x114>{});   // row_shr:4
+  x += shr(x, std::integral_constant<int, 0x118>{});   // row_shr:8
+  // row_bcast:15 into rows 1 and 3 (lane 15 of the row below)
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
+  return x;
+}
+
+// Lane q of each aligned group of W lanes (W = 1, 2 or 4) to the whole group.
+template <int W, int Q>
+__device__ __forceinline__ float group_bcast(float x) {
+  if constexpr (W == 1 || Q >= W) return x;   // Q >= W: never selected
+  else {
+    constexpr int s0 = Q, s1 = W == 4 ? Q : Q, s2 = W == 4 ? Q : 2 + Q, s3 = W == 4 ? Q : 2 + Q;
+    constexpr int ctrl = s0 | (s1 << 2) | (s2 << 4) | (s3 << 6);   // quad_perm
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
+  }
+}
+
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ void store_split(uint16_t* hi_plane, int plane_stride, int idx, float x) {
@@ -111,31 +139,40 @@ __device__ __forceinline__ void store_split(uint16_t* hi_plane, int plane_stride
 // Row of accumulator register i for lane half g.
 __device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
 
-template <int DK, int DV, int NT>
+template <int DK, int DV>
 struct Cfg {
-  static constexpr int CT = 32 * NT;      // rows of the chunk tile
+  static constexpr int CT = 32;           // tokens per chunk tile
   static constexpr int NW = DV / 32;      // waves
   static constexpr int NTH = 64 * NW;     // threads
   static constexpr int KT = DK / 32;      // 32-wide k tiles of the state
   static constexpr int LDK = DK + 4;      // row stride of sK, sQ (bf16; 8-byte aligned rows)
+  static constexpr int LDKT = CT + 4;     // row stride of sKt, the transposed K tile (bf16)
   static constexpr int LDT = CT + 4;      // row stride of sT, sP (bf16)
-  // forward substitution: LPC lanes per column of the diagonal blocks
-  static constexpr int LPC_RAW = NTH / CT;
+  static constexpr int LDV = DV + 8;      // row stride of the V / O tile (bf16; 16-byte rows)
+  static constexpr int LDA = CT + 4;      // row stride of sA, A transposed (fp32)
+  // With four waves, waves 2 and 3 run the substitution while waves 0 and 1
+  // form their K S0^T and Q S0^T (waves 2 and 3 formed theirs during the
+  // Gram stage); with fewer, every wave forms them after the substitution.
+  static constexpr bool SPLIT = NW >= 4;
+  static constexpr int SUB0 = SPLIT ? 128 : 0;       // first substitution thread
+  static constexpr int SUBT = SPLIT ? 128 : NTH;     // substitution threads available
+  // forward substitution: LPC lanes per column of T
+  static constexpr int LPC_RAW = SUBT / CT;
   static constexpr int LPC = LPC_RAW > 4 ? 4 : (LPC_RAW < 1 ? 1 : LPC_RAW);
-  static constexpr int MPL = 32 / LPC;    // rows of a column held per lane
-  static constexpr int LDA = 32 + 4;      // row stride of a diagonal block of A (fp32)
+  static constexpr int MPL = CT / LPC;    // rows of a column held per lane
   static constexpr int oK = 0;
   static constexpr int oQ = oK + CT * LDK * 2;
-  static constexpr int LDV = DV + 8;      // row stride of the V / O tile (bf16; 16-byte rows)
-  static constexpr int oV = oQ + CT * LDK * 2;        // V tile, then the O tile
-  static constexpr int oT = oV + CT * LDV * 2;        // hi then lo plane: T11, -A21, T22
+  static constexpr int oKt = oQ + CT * LDK * 2;
+  static constexpr int oV = oKt + DK * LDKT * 2;      // V tile, then the O tile
+  static constexpr int oT = oV + CT * LDV * 2;        // hi then lo plane
   static constexpr int oP = oT + 2 * CT * LDT * 2;    // hi then lo plane
-  static constexpr int oA = oP + 2 * CT * LDT * 2;    // NT diagonal blocks of A, lane-interleaved
-  static constexpr int oS = oA + NT * 32 * LDA * 4;   // per-token scalars
+  static constexpr int oA = oP + 2 * CT * LDT * 2;
+  static constexpr int oS = oA + CT * LDA * 4;        // per-token scalars
   static constexpr int kScal = 8;
   static constexpr int bytes = oS + kScal * CT * 4;
   static_assert(bytes <= 80 * 1024, "two workgroups per CU");
-  static_assert(LPC * CT <= NTH || LPC == 1, "substitution lanes");
+  static_assert(NW <= 4 && LPC * CT <= SUBT, "wave roles");
+  static_assert(oQ % 16 == 0 && oKt % 16 == 0 && oV % 16 == 0 && oT % 16 == 0 && oA % 16 == 0, "align");
   // the next chunk's rows wait in registers (16-byte vectors per thread)
   // while this chunk computes, when they fit in 32 registers
   static constexpr int NVK = (CT * DK / 8 + NTH - 1) / NTH;
@@ -146,21 +183,22 @@ struct Cfg {
 // per-token scalar arrays (index into the scalar block)
 enum { SC_G = 0, SC_BETA, SC_RK, SC_RQ, SC_CK, SC_CQ, SC_CU, SC_PAD };
 
-template <int DK, int DV, int NT>
+template <int DK, int DV>
 __global__ void __launch_bounds__(64 * (DV / 32), 2)
 chunked_prefill_kernel(const ScanArgs a) {
-  using C = Cfg<DK, DV, NT>;
-  constexpr int CT = C::CT, NTH = C::NTH, KT = C::KT, LDK = C::LDK, LDT = C::LDT, LDA = C::LDA;
-  constexpr int LPC = C::LPC, MPL = C::MPL, LDV = C::LDV;
+  using C = Cfg<DK, DV>;
+  constexpr int CT = C::CT, NTH = C::NTH, KT = C::KT, LDK = C::LDK, LDKT = C::LDKT, LDT = C::LDT;
+  constexpr int LDA = C::LDA, LPC = C::LPC, MPL = C::MPL, LDV = C::LDV;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* sK = reinterpret_cast<uint16_t*>(smem + C::oK);
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + C::oQ);
+  uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + C::oKt);
   uint16_t* sV = reinterpret_cast<uint16_t*>(smem + C::oV);
   uint16_t* sT = reinterpret_cast<uint16_t*>(smem + C::oT);
   uint16_t* sP = reinterpret_cast<uint16_t*>(smem + C::oP);
   float* sA = reinterpret_cast<float*>(smem + C::oA);
   float* sc = reinterpret_cast<float*>(smem + C::oS);
-  float* sG = sc + SC_G * CT;       // raw log-gates, then their cumsum
+  float* sG = sc + SC_G * CT;       // cumsum of the log-gates
   float* sBeta = sc + SC_BETA * CT;
   float* sRk = sc + SC_RK * CT;
   float* sRq = sc + SC_RQ * CT;
@@ -216,25 +254,33 @@ chunked_prefill_kernel(const ScanArgs a) {
   // One chunk's HBM rows into registers.  Every lane loads (row index clamped
   // into the chunk, so no load is conditional); rows past the chunk's end are
   // zeroed where they are consumed.
-  u32x4 pk[C::NVK], pq[C::NVK], pv[C::NVV];
+  auto ld_kq = [&](int u, int t0x, int nx, u32x4& kx, u32x4& qx) {
+    const int e = min(tid + u * NTH, CT * DK / 8 - 1);
+    const int t = min(e / (DK / 8), nx - 1), c8 = (e % (DK / 8)) * 8;
+    kx = *reinterpret_cast<const u32x4*>(kg + (size_t)(t0x + t) * a.k_stride + (size_t)j * DK + c8);
+    qx = *reinterpret_cast<const u32x4*>(qg + (size_t)(t0x + t) * a.q_stride + (size_t)j * DK + c8);
+  };
+  auto ld_v = [&](int u, int t0x, int nx, u32x4& vx) {
+    const int e = min(tid + u * NTH, CT * DV / 8 - 1);
+    const int t = min(e / (DV / 8), nx - 1), c8 = (e % (DV / 8)) * 8;
+    vx = *reinterpret_cast<const u32x4*>(vg + (size_t)(t0x + t) * a.v_stride + c8);
+  };
+  auto ld_gb = [&](int t0x, int nx, float& gx, float& bx) {
+    const int tl = min(lane, nx - 1);
+    gx = a.g[(size_t)(t0x + tl) * a.Hv + h];
+    bx = a.beta[(size_t)(t0x + tl) * a.Hv + h];
+  };
+  // with PREFETCH the rows of the next chunk are held here between chunks;
+  // otherwise each vector is loaded where it is consumed
+  constexpr int NPK = C::PREFETCH ? C::NVK : 1, NPV = C::PREFETCH ? C::NVV : 1;
+  u32x4 pk[NPK], pq[NPK], pv[NPV];
   float pg, pb;
   auto fetch = [&](int t0x, int nx) {
 #pragma unroll
-    for (int u = 0; u < C::NVK; ++u) {
-      const int e = min(tid + u * NTH, CT * DK / 8 - 1);
-      const int t = min(e / (DK / 8), nx - 1), c8 = (e % (DK / 8)) * 8;
-      pk[u] = *reinterpret_cast<const u32x4*>(kg + (size_t)(t0x + t) * a.k_stride + (size_t)j * DK + c8);
-      pq[u] = *reinterpret_cast<const u32x4*>(qg + (size_t)(t0x + t) * a.q_stride + (size_t)j * DK + c8);
-    }
+    for (int u = 0; u < NPK; ++u) ld_kq(u, t0x, nx, pk[u], pq[u]);
 #pragma unroll
-    for (int u = 0; u < C::NVV; ++u) {
-      const int e = min(tid + u * NTH, CT * DV / 8 - 1);
-      const int t = min(e / (DV / 8), nx - 1), c8 = (e % (DV / 8)) * 8;
-      pv[u] = *reinterpret_cast<const u32x4*>(vg + (size_t)(t0x + t) * a.v_stride + c8);
-    }
-    const int tl = min(lane, nx - 1);
-    pg = a.g[(size_t)(t0x + tl) * a.Hv + h];
-    pb = a.beta[(size_t)(t0x + tl) * a.Hv + h];
+    for (int u = 0; u < NPV; ++u) ld_v(u, t0x, nx, pv[u]);
+    ld_gb(t0x, nx, pg, pb);
   };
   if constexpr (C::PREFETCH)
     if (seq1 > seq0) fetch(seq0, min(a.chunk, seq1 - seq0));
@@ -242,17 +288,77 @@ chunked_prefill_kernel(const ScanArgs a) {
   // chunk loop has to cover them (vmcnt(0); expcnt, lgkmcnt unchanged)
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
+  // Operands of a chain over the full key dimension: with several waves
+  // every row operand is read before the MFMA chain starts (registers are
+  // free then); a single wave holds more live state, so it reads them as it
+  // goes.
+  constexpr bool PRE = C::NW > 1;
+  constexpr int NKS = PRE ? DK / 16 : 1;
+
+  // X = K S0^T and QS = Q S0^T for this wave's columns, S0 split per k tile
+  // on the fly
+  auto xqs = [&](f32x16& X, f32x16& QS) {
+    bf16x8 ka[NKS], qa[NKS];
+    auto ld = [&](int ks, bf16x8& kx, bf16x8& qx) {
+      const int off = c * LDK + 4 * g + 16 * ks;
+      kx = lds_op(sK + off);
+      qx = lds_op(sQ + off);
+    };
+    if constexpr (PRE)
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks) ld(ks, ka[ks], qa[ks]);
+    X = f32x16{};
+    QS = f32x16{};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int ks = 2 * kt + h2;
+        if constexpr (!PRE) ld(ks, ka[0], qa[0]);
+        const bf16x8& kx = ka[PRE ? ks : 0];
+        const bf16x8& qx = qa[PRE ? ks : 0];
+        bf16x8 sh, sl;
+        if (h2 == 0) split_half<0>(S[kt], sh, sl); else split_half<1>(S[kt], sh, sl);
+        X = mma(kx, sh, X);
+        X = mma(kx, sl, X);
+        QS = mma(qx, sh, QS);
+        QS = mma(qx, sl, QS);
+      }
+  };
+
+  // Gram-type tile: sum over k of (row c of xa) (row c of xb), the A operand
+  // rows giving the accumulator rows and the B operand rows its columns
+  auto rows_mm = [&](const uint16_t* xa, const uint16_t* xb) {
+    bf16x8 ar[NKS], br[NKS];
+    if constexpr (PRE)
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks) {
+        ar[ks] = lds_op(xa + c * LDK + 4 * g + 16 * ks);
+        br[ks] = lds_op(xb + c * LDK + 4 * g + 16 * ks);
+      }
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < DK / 16; ++ks) {
+      if constexpr (!PRE) {
+        ar[0] = lds_op(xa + c * LDK + 4 * g + 16 * ks);
+        br[0] = lds_op(xb + c * LDK + 4 * g + 16 * ks);
+      }
+      acc = mma(ar[PRE ? ks : 0], br[PRE ? ks : 0], acc);
+    }
+    return acc;
+  };
+
   int pt0 = 0, pn = 0;   // previous chunk: its O tile is still in the V/O LDS tile
   for (int t0 = seq0; t0 < seq1; t0 += a.chunk) {
     const int n = min(a.chunk, seq1 - t0);   // valid rows of this chunk
 
-    // ---- 1. stage K, Q rows (zero past n) with their L2 norms (squares summed
-    //         in registers, then over the row's lanes), V rows, betas and the
-    //         gate cumsum.  The rows were fetched into registers while the
-    //         previous chunk ran.  The previous chunk's O rows leave the V/O
-    //         tile first: read into registers before V lands, stored to HBM
-    //         after (global stores issued after the loads are consumed).
-    if constexpr (!C::PREFETCH) fetch(t0, n);
+    // ---- 1. stage K (row-major and transposed) and Q rows (zero past n)
+    //         with their L2 norms (squares summed in registers, then over
+    //         the row's lanes), V rows, betas and the gate cumsum.  The rows
+    //         were fetched into registers while the previous chunk ran.  The
+    //         previous chunk's O rows leave the V/O tile first: read into
+    //         registers before V lands, stored to HBM after.
+    if constexpr (!C::PREFETCH) ld_gb(t0, n, pg, pb);
     {
       constexpr int VPR = DK / 8;          // 16-byte vectors per row = lanes per row
       static_assert((CT * DK / 8) % 64 == 0 && VPR <= 16, "row lanes");
@@ -261,19 +367,27 @@ chunked_prefill_kernel(const ScanArgs a) {
         const int e = tid + u * NTH;
         if (e < CT * DK / 8) {             // whole waves per trip
           const int t = e / VPR, c8 = (e % VPR) * 8;
+          u32x4 kx, qx;
+          if constexpr (C::PREFETCH) { kx = pk[u]; qx = pq[u]; } else ld_kq(u, t0, n, kx, qx);
           const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 kv = t < n ? pk[u] : z, qv = t < n ? pq[u] : z;
+          const u32x4 kv = t < n ? kx : z, qv = t < n ? qx : z;
           u32x2* kd = reinterpret_cast<u32x2*>(sK + t * LDK + c8);
           u32x2* qd = reinterpret_cast<u32x2*>(sQ + t * LDK + c8);
           kd[0] = u32x2{kv.x, kv.y}; kd[1] = u32x2{kv.z, kv.w};
           qd[0] = u32x2{qv.x, qv.y}; qd[1] = u32x2{qv.z, qv.w};
+          const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+          for (int p2 = 0; p2 < 4; ++p2) {
+            sKt[(c8 + 2 * p2) * LDKT + t] = (uint16_t)(kw[p2] & 0xFFFFu);
+            sKt[(c8 + 2 * p2 + 1) * LDKT + t] = (uint16_t)(kw[p2] >> 16);
+          }
           float sk = sumsq8(kv), sq = sumsq8(qv);
           sk = group_sum<VPR>(sk);
           sq = group_sum<VPR>(sq);
           if (e % VPR == 0) {   // zero-padded rows past n keep r = 1 (no 0 * inf)
             const bool nrm = a.l2norm && t < n;
-            sRk[t] = nrm ? 1.0f / sqrtf(sk + a.eps) : 1.0f;
-            sRq[t] = nrm ? 1.0f / sqrtf(sq + a.eps) : 1.0f;
+            sRk[t] = nrm ? __builtin_amdgcn_rsqf(sk + a.eps) : 1.0f;
+            sRq[t] = nrm ? __builtin_amdgcn_rsqf(sq + a.eps) : 1.0f;
           }
         }
       }
@@ -287,17 +401,14 @@ chunked_prefill_kernel(const ScanArgs a) {
         if (e < CT * DV / 8) {
           const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
           u32x4* seg = reinterpret_cast<u32x4*>(sV + t * LDV + c8);
+          u32x4 vx;
+          if constexpr (C::PREFETCH) vx = pv[u]; else ld_v(u, t0, n, vx);
           ov[u] = *seg;
-          *seg = t < n ? pv[u] : u32x4{0u, 0u, 0u, 0u};
+          *seg = t < n ? vx : u32x4{0u, 0u, 0u, 0u};
         }
       }
       if (wave == 0) {  // betas and the inclusive scan of the log-gates (fixed order)
-        float x = lane < n ? pg : 0.f;
-#pragma unroll
-        for (int d = 1; d < CT; d <<= 1) {
-          const float y = __shfl_up(x, d, 64);
-          if (lane >= d) x += y;
-        }
+        const float x = scan32(lane < n ? pg : 0.f);
         if (lane < CT) {
           sG[lane] = x;
           sBeta[lane] = lane < n ? pb : 0.f;
@@ -315,121 +426,144 @@ chunked_prefill_kernel(const ScanArgs a) {
     if constexpr (C::PREFETCH)
       if (t0 + a.chunk < seq1) fetch(t0 + a.chunk, min(a.chunk, seq1 - t0 - a.chunk));
 
-    // ---- 3. Gram and Q K^T tiles (MFMA, shared K operand) -> A, P; scalars
-    {
-      constexpr int NTILE = NT * (NT + 1) / 2;
-      for (int job = wave; job < 2 * NTILE; job += C::NW) {
-        const bool gram = job < NTILE;                 // Gram K K^T, else Q K^T
-        const int tix = gram ? job : job - NTILE;
-        const int mt = tix == 0 ? 0 : 1, nt = tix == 2 ? 1 : 0;
-        const uint16_t* ar = (gram ? sK : sQ) + (32 * mt + c) * LDK + 4 * g;
-        const uint16_t* br = sK + (32 * nt + c) * LDK + 4 * g;
-        f32x16 acc = {};
+    f32x16 X, QS;   // K S0^T, Q S0^T for this wave's columns
+    // ---- 3. Gram tile -> A (wave 0), K Q^T tile -> P (wave 1), per-token
+    //         scalars (wave 0); waves 2, 3 form their X and QS meanwhile.
+    //         Row operands are read before each MFMA chain.
+    if (wave == 0) {
+      // Gram K K^T: both operands are the K rows (lane column = key i = c,
+      // accumulator rows = token t); A[t][i] = beta_t r_t r_i e^{G_t - G_i} k_t.k_i
+      // for i < t, stored transposed with rows interleaved over the LPC lane
+      // parts of the substitution: (t, i) at i*LDA + (t % LPC)*MPL + t / LPC
+      const f32x16 acc = rows_mm(sK, sK);
+      const float gi = sG[c], ri = sRk[c];
 #pragma unroll
-        for (int ks = 0; ks < DK / 16; ++ks) acc = mma(lds_op(ar + 16 * ks), lds_op(br + 16 * ks), acc);
-        const int col = 32 * nt + c, lcol = c;   // global / block-local column
-        const float gc = sG[col], rkc = sRk[col];
-        const int qa = lcol % LPC, ma = lcol / LPC;
-        const float* rowsc = gram ? sRk : sRq;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int tb = 8 * q4 + 4 * g;
+        const float4 G4 = *reinterpret_cast<const float4*>(sG + tb);
+        const float4 B4 = *reinterpret_cast<const float4*>(sBeta + tb);
+        const float4 R4 = *reinterpret_cast<const float4*>(sRk + tb);
+        const float Gr[4] = {G4.x, G4.y, G4.z, G4.w}, Br[4] = {B4.x, B4.y, B4.z, B4.w};
+        const float Rr[4] = {R4.x, R4.y, R4.z, R4.w};
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int tb = 32 * mt + 8 * q4 + 4 * g;
-          const float4 G4 = *reinterpret_cast<const float4*>(sG + tb);
-          const float4 B4 = *reinterpret_cast<const float4*>(sBeta + tb);
-          const float4 R4 = *reinterpret_cast<const float4*>(rowsc + tb);
-          const float Gr[4] = {G4.x, G4.y, G4.z, G4.w}, Br[4] = {B4.x, B4.y, B4.z, B4.w};
-          const float Rr[4] = {R4.x, R4.y, R4.z, R4.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = tb + r;
-            const bool on = gram ? col < t : col <= t;
-            const float dcy = __expf(on ? Gr[r] - gc : 0.f);
-            const float f = (gram ? Br[r] : a.scale) * Rr[r] * rkc * dcy * acc[4 * q4 + r];
-            const float val = on ? f : 0.f;
-            if (!gram) store_split(sP, TPL, t * LDT + col, val);
-            else if (mt == nt) sA[t * LDA + qa * MPL + ma] = val;
-            else store_split(sT, TPL, t * LDT + col, -val);      // -A21, split operand
-          }
+        for (int r = 0; r < 4; ++r) {
+          const int t = tb + r;
+          const bool on = c < t;
+          const float f = Br[r] * Rr[r] * ri * __expf(on ? Gr[r] - gi : 0.f) * acc[4 * q4 + r];
+          sA[c * LDA + (t % LPC) * MPL + t / LPC] = on ? f : 0.f;
         }
       }
-      if (tid < CT) {
-        const float G = sG[tid], GC = sG[CT - 1];
-        sCk[tid] = sRk[tid] * __expf(G);
-        sCq[tid] = a.scale * sRq[tid] * __expf(G);
-        sCu[tid] = sRk[tid] * __expf(GC - G);
+      if (lane < CT) {
+        const float G = sG[lane], GC = sG[CT - 1];
+        sCk[lane] = sRk[lane] * __expf(G);
+        sCq[lane] = a.scale * sRq[lane] * __expf(G);
+        sCu[lane] = sRk[lane] * __expf(GC - G);
       }
     }
+    if (wave == (C::NW > 1 ? 1 : 0)) {
+      // K Q^T: A operand = K rows (accumulator row = key i), B operand = Q
+      // rows (lane column = query t = c); P[t][i] = scale r_q,t r_k,i
+      // e^{G_t - G_i} q_t.k_i for i <= t, written as row t of P (hi and lo
+      // planes), four keys per 8-byte store
+      const f32x16 acc = rows_mm(sK, sQ);
+      const float gt = sG[c], rt = a.scale * sRq[c];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int ib = 8 * q4 + 4 * g;
+        const float4 G4 = *reinterpret_cast<const float4*>(sG + ib);
+        const float4 R4 = *reinterpret_cast<const float4*>(sRk + ib);
+        const float Gi[4] = {G4.x, G4.y, G4.z, G4.w}, Ri[4] = {R4.x, R4.y, R4.z, R4.w};
+        float pv4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool on = ib + r <= c;
+          const float f = rt * Ri[r] * __expf(on ? gt - Gi[r] : 0.f) * acc[4 * q4 + r];
+          pv4[r] = on ? f : 0.f;
+        }
+        uint32_t h01, l01, h23, l23;
+        split2(pv4[0], pv4[1], h01, l01);
+        split2(pv4[2], pv4[3], h23, l23);
+        *reinterpret_cast<u32x2*>(sP + c * LDT + ib) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(sP + TPL + c * LDT + ib) = u32x2{l01, l23};
+      }
+    }
+    if constexpr (C::SPLIT)
+      if (wave >= 2) xqs(X, QS);
     __syncthreads();
 
-    // ---- 4. diagonal blocks T_bb = (I + A_bb)^-1 by forward substitution.
-    //         LPC consecutive lanes share column jj: lane part q keeps rows
-    //         q, q+LPC, ... of the column and sums their terms; a row's total
-    //         is a fixed-order lane-group sum.
-    if (tid < CT * LPC) {
-      const int jj = tid / LPC, q = tid % LPC;
-      const int b = jj >> 5, cc = jj & 31;
-      const float* ab = sA + 32 * b * LDA + q * MPL;
+    // ---- 4. T = (I + A)^-1 by right-looking forward substitution: column jj
+    //         of T is spread over LPC consecutive lanes, lane part q keeping
+    //         rows q, q+LPC, ... as running sums delta(r, jj) - sum_{i<r}
+    //         A[r][i] T[i][jj].  At step i the owner lane's sum for row i is
+    //         final; it is broadcast to the group and every lane folds it into
+    //         its later rows (A's zero upper part leaves finished rows alone).
+    //         A is stored transposed, so the column read at step i is
+    //         contiguous per lane part.
+    if (tid >= C::SUB0 && tid < C::SUB0 + CT * LPC) {
+      const int st = tid - C::SUB0;
+      const int jj = st / LPC, q = st % LPC;
+      const float* ab = sA + q * MPL;
       float Tl[MPL];
 #pragma unroll
-      for (int m = 0; m < MPL; ++m) Tl[m] = 0.f;
+      for (int m = 0; m < MPL; ++m) Tl[m] = (q + LPC * m == jj) ? 1.f : 0.f;
+      // columns of A come in batches of SB steps, one batch ahead of use, so
+      // the LDS latency is not paid step by step
+      constexpr int SB = MPL <= 8 ? 4 : (MPL == 16 ? 2 : 1), NB = CT / SB;   // SB * MPL <= 32
+      float col[2][SB][MPL];
+      auto load_batch = [&](float (&dst)[SB][MPL], int bt) {
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
-        float acc0 = 0.f, acc1 = 0.f;
-        const float* arow = ab + t * LDA;
+        for (int u = 0; u < SB; ++u)
 #pragma unroll
-        for (int m = 0; m < (t + LPC - 1) / LPC; ++m) {
-          if (m & 1) acc1 = fmaf(-arow[m], Tl[m], acc1);
-          else acc0 = fmaf(-arow[m], Tl[m], acc0);
+          for (int m4 = 0; m4 < MPL; m4 += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(ab + (SB * bt + u) * LDA + m4);
+            dst[u][m4] = x.x; dst[u][m4 + 1] = x.y; dst[u][m4 + 2] = x.z; dst[u][m4 + 3] = x.w;
+          }
+      };
+      load_batch(col[0], 0);
+#pragma unroll
+      for (int bt = 0; bt < NB; ++bt) {
+        if (bt + 1 < NB) load_batch(col[(bt + 1) & 1], bt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {   // unrolled: t % LPC and t / LPC are constants
+          const int t = SB * bt + u;
+          if (t < CT - 1) {
+            const float own = Tl[t / LPC];
+            const int qt = t % LPC;
+            const float Tt = qt == 0 ? group_bcast<LPC, 0>(own)
+                           : qt == 1 ? group_bcast<LPC, 1>(own)
+                           : qt == 2 ? group_bcast<LPC, 2>(own) : group_bcast<LPC, 3>(own);
+#pragma unroll
+            for (int m = t / LPC; m < MPL; ++m) Tl[m] = fmaf(-col[bt & 1][u][m], Tt, Tl[m]);
+          }
         }
-        const float tot = group_sum<LPC>(acc0 + acc1) + (t == cc ? 1.f : 0.f);
-        if (q == t % LPC) Tl[t / LPC] = tot;
+        __builtin_amdgcn_sched_barrier(0);
       }
-      uint16_t* tb = sT + 32 * b * LDT + 32 * b + cc;
+      uint16_t* tcol = sT + jj;
 #pragma unroll
-      for (int m = 0; m < MPL; ++m) store_split(tb, TPL, (q + LPC * m) * LDT, Tl[m]);
+      for (int m = 0; m < MPL; ++m) store_split(tcol, TPL, (q + LPC * m) * LDT, Tl[m]);
     }
+    if constexpr (C::SPLIT)
+      if (wave < 2) xqs(X, QS);
     __syncthreads();
 
     // ---- 5. state path for this wave's 32 value columns
+    if constexpr (!C::SPLIT) xqs(X, QS);
     {
-      // X = K S0^T and QS = Q S0^T, S0 split per k tile on the fly
-      f32x16 X[NT], QS[NT];
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt) { X[mt] = f32x16{}; QS[mt] = f32x16{}; }
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          bf16x8 sh, sl;
-          if (h2 == 0) split_half<0>(S[kt], sh, sl); else split_half<1>(S[kt], sh, sl);
-#pragma unroll
-          for (int mt = 0; mt < NT; ++mt) {
-            const int off = (32 * mt + c) * LDK + 4 * g + 32 * kt + 16 * h2;
-            const bf16x8 ka = lds_op(sK + off);
-            const bf16x8 qa = lds_op(sQ + off);
-            X[mt] = mma(ka, sh, X[mt]);
-            X[mt] = mma(ka, sl, X[mt]);
-            QS[mt] = mma(qa, sh, QS[mt]);
-            QS[mt] = mma(qa, sl, QS[mt]);
-          }
-        }
       // Y = beta (V - r_k e^G X), in place of X (zero past n)
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int tb = 8 * q4 + 4 * g;
+        const float4 b4 = *reinterpret_cast<const float4*>(sBeta + tb);
+        const float4 k4 = *reinterpret_cast<const float4*>(sCk + tb);
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int tb = 32 * mt + 8 * q4 + 4 * g;
-          const float4 b4 = *reinterpret_cast<const float4*>(sBeta + tb);
-          const float4 k4 = *reinterpret_cast<const float4*>(sCk + tb);
-          const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * q4 + r;
-            const float vvv = bf16_to_f32(sV[(tb + r) * LDV + v]);
-            const float y = bb[r] * (vvv - kk[r] * X[mt][i]);
-            X[mt][4 * q4 + r] = tb + r < n ? y : 0.f;
-          }
+        for (int r = 0; r < 4; ++r) {
+          const float vvv = bf16_to_f32(sV[(tb + r) * LDV + v]);
+          const float y = bb[r] * (vvv - kk[r] * X[4 * q4 + r]);
+          X[4 * q4 + r] = tb + r < n ? y : 0.f;
         }
+      }
       // product of a split 32x32 LDS block (rows at rowp) with a split tile
       auto tri_mm = [&](const uint16_t* rowp, const uint16_t* lo_plane_rowp, const f32x16& y,
                         f32x16 acc) {
@@ -446,68 +580,51 @@ chunked_prefill_kernel(const ScanArgs a) {
         acc = mma(a1h, yl1, acc);
         return acc;
       };
-      // U1 = T11 Y1;  U2 = T22 (Y2 - A21 U1)
-      f32x16 U[NT];
-      {
-        const uint16_t* r0 = sT + c * LDT + 4 * g;
-        U[0] = tri_mm(r0, r0 + TPL, X[0], f32x16{});
-        if constexpr (NT == 2) {
-          const uint16_t* r1 = sT + (32 + c) * LDT + 4 * g;
-          const f32x16 w = tri_mm(r1, r1 + TPL, U[0], X[1]);
-          U[1] = tri_mm(r1 + 32, r1 + 32 + TPL, w, f32x16{});
-        }
+      // U = T Y
+      const uint16_t* tr = sT + c * LDT + 4 * g;
+      f32x16 U = tri_mm(tr, tr + TPL, X, f32x16{});
+      // O = scale r_q e^G (Q S0^T) + P U, into this wave's own columns of the
+      // V/O tile (V of these columns was consumed above by this wave only);
+      // stored out next chunk
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 c4 = *reinterpret_cast<const float4*>(sCq + 8 * q4 + 4 * g);
+        QS[4 * q4] *= c4.x; QS[4 * q4 + 1] *= c4.y;
+        QS[4 * q4 + 2] *= c4.z; QS[4 * q4 + 3] *= c4.w;
       }
-      // O = scale r_q e^G (Q S0^T) + P U -> out rows < n
+      const uint16_t* pr = sP + c * LDT + 4 * g;
+      QS = tri_mm(pr, pr + TPL, U, QS);
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 c4 = *reinterpret_cast<const float4*>(sCq + 32 * mt + 8 * q4 + 4 * g);
-          QS[mt][4 * q4] *= c4.x; QS[mt][4 * q4 + 1] *= c4.y;
-          QS[mt][4 * q4 + 2] *= c4.z; QS[mt][4 * q4 + 3] *= c4.w;
-        }
-        const uint16_t* pr = sP + (32 * mt + c) * LDT + 4 * g;
-#pragma unroll
-        for (int m2 = 0; m2 <= mt; ++m2) QS[mt] = tri_mm(pr + 32 * m2, pr + 32 * m2 + TPL, U[m2], QS[mt]);
-        // O into this wave's own columns of the V/O tile (V of these columns
-        // was consumed above by this wave only); stored out next chunk
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sV[(32 * mt + acc_row(i, g)) * LDV + v] = bf16_bits(QS[mt][i]);
-      }
-      // S = e^{G_C} S + K^T (r_k e^{G_C - G} U); K^T operand gathered from K rows
+      for (int i = 0; i < 16; ++i) sV[acc_row(i, g) * LDV + v] = bf16_bits(QS[i]);
+      // S = e^{G_C} S + K^T (r_k e^{G_C - G} U); K^T rows from the transposed tile
       const float gC = __expf(sG[CT - 1]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[kt][i] *= gC;
 #pragma unroll
-      for (int m2 = 0; m2 < NT; ++m2) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 c4 = *reinterpret_cast<const float4*>(sCu + 32 * m2 + 8 * q4 + 4 * g);
-          U[m2][4 * q4] *= c4.x; U[m2][4 * q4 + 1] *= c4.y;
-          U[m2][4 * q4 + 2] *= c4.z; U[m2][4 * q4 + 3] *= c4.w;
-        }
-        bf16x8 uh[2], ul[2];
-        split_half<0>(U[m2], uh[0], ul[0]);
-        split_half<1>(U[m2], uh[1], ul[1]);
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            // A operand: rows k = 32kt + c, k-order (tokens) 32*m2 + 16*h2 + 4g + {0..3, 8..11}
-            const uint16_t* kc = sK + (32 * m2 + 16 * h2 + 4 * g) * LDK + 32 * kt + c;
-            uint32_t w[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const int r = (p < 2 ? 0 : 8) + 2 * (p & 1);
-              w[p] = (uint32_t)kc[r * LDK] | ((uint32_t)kc[(r + 1) * LDK] << 16);
-            }
-            const bf16x8 ka = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-            S[kt] = mma(ka, uh[h2], S[kt]);
-            S[kt] = mma(ka, ul[h2], S[kt]);
-          }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 c4 = *reinterpret_cast<const float4*>(sCu + 8 * q4 + 4 * g);
+        U[4 * q4] *= c4.x; U[4 * q4 + 1] *= c4.y;
+        U[4 * q4 + 2] *= c4.z; U[4 * q4 + 3] *= c4.w;
       }
+      bf16x8 uh[2], ul[2];
+      split_half<0>(U, uh[0], ul[0]);
+      split_half<1>(U, uh[1], ul[1]);
+      bf16x8 kta[NKS];
+      auto ldt = [&](int kt, int h2) { return lds_op(sKt + (32 * kt + c) * LDKT + 16 * h2 + 4 * g); };
+      if constexpr (PRE)
+#pragma unroll
+        for (int ks = 0; ks < DK / 16; ++ks) kta[ks] = ldt(ks / 2, ks % 2);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          if constexpr (!PRE) kta[0] = ldt(kt, h2);
+          const bf16x8& kx = kta[PRE ? 2 * kt + h2 : 0];
+          S[kt] = mma(kx, uh[h2], S[kt]);
+          S[kt] = mma(kx, ul[h2], S[kt]);
+        }
     }
     if (t0 + n == next_ck) {
       store_state(a.ckpt_buf + (size_t)ci * sstride + ((size_t)h * DV + v) * DK);
@@ -530,33 +647,28 @@ chunked_prefill_kernel(const ScanArgs a) {
 }  // namespace chunked
 }  // namespace gdn
 
-// Instantiates the launchers for one key dimension.
+// Instantiates the launchers for one key dimension.  The scan runs 32-token
+// chunks for chunk = 32 or 64 (a checkpoint on the 64-grid is on the 32-grid
+// too) and 16-token chunks, zero-padded in the 32-row tile, for chunk = 16.
 #define GDN_CHUNKED_LAUNCHERS(DKV)                                                          \
   namespace gdn {                                                                          \
   namespace chunked {                                                                      \
-  template <int DV, int NT>                                                                \
+  template <int DV>                                                                        \
   static hipError_t launch_one(const ScanArgs& a, hipStream_t st) {                        \
-    using C = Cfg<DKV, DV, NT>;                                                            \
-    auto kern = chunked_prefill_kernel<DKV, DV, NT>;                                       \
+    using C = Cfg<DKV, DV>;                                                                \
+    auto kern = chunked_prefill_kernel<DKV, DV>;                                           \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::bytes); \
     if (e != hipSuccess) return e;                                                         \
-    hipLaunchKernelGGL(kern, dim3(a.n_seqs, a.Hv), dim3(C::NTH), C::bytes, st, a);         \
+    ScanArgs b = a;                                                                        \
+    b.chunk = a.chunk > C::CT ? C::CT : a.chunk;                                           \
+    hipLaunchKernelGGL(kern, dim3(b.n_seqs, b.Hv), dim3(C::NTH), C::bytes, st, b);         \
     return hipGetLastError();                                                              \
   }                                                                                        \
-  /* The scan runs 32-token chunks for chunk = 32 or 64 (a 64-grid checkpoint  */         \
-  /* is on the 32-grid too) and 16-token chunks, zero-padded, for chunk = 16:  */         \
-  /* the 64-row tile needs more than the 256 registers of two workgroups/CU.   */         \
-  template <int DV>                                                                        \
-  static hipError_t launch_nt(const ScanArgs& a, hipStream_t st) {                         \
-    ScanArgs b = a;                                                                        \
-    b.chunk = a.chunk > 32 ? 32 : a.chunk;                                                 \
-    return launch_one<DV, 1>(b, st);                                                       \
-  }                                                                                        \
   hipError_t launch_dk##DKV(const ScanArgs& a, hipStream_t st) {                           \
-    if (a.dv == 32) return launch_nt<32>(a, st);                                           \
-    if (a.dv == 64) return launch_nt<64>(a, st);                                           \
-    if (a.dv == 128) return launch_nt<128>(a, st);                                         \
+    if (a.dv == 32) return launch_one<32>(a, st);                                          \
+    if (a.dv == 64) return launch_one<64>(a, st);                                          \
+    if (a.dv == 128) return launch_one<128>(a, st);                                        \
     return hipErrorInvalidValue;                                                           \
   }                                                                                        \
   }                                                                                        \
