@@ -215,6 +215,50 @@ def bench_snapshot(torch, gdn, stream, flush, reps):
             "exact": ok}
 
 
+def _pinned_device_address(t) -> int:
+    """Device address of a pinned host tensor (hipHostGetDevicePointer)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    d = ctypes.c_void_p()
+    rc = hip.hipHostGetDevicePointer(ctypes.byref(d), ctypes.c_void_p(t.data_ptr()), 0)
+    if rc != 0 or not d.value:
+        raise RuntimeError(f"hipHostGetDevicePointer returned {rc}")
+    return d.value
+
+
+def bench_prefix_cache(torch, gdn, stream, flush, reps):
+    """Checkpoint gather into a pinned host pool allocated once (device writes
+    over the host link), then the H2D restore of 32 states into init_state."""
+    n, Hv, d = 96, 32, 128
+    src = torch.randn((n, Hv, d, d), device="cuda:0")
+    pool = torch.zeros((n + 32, Hv, d, d), dtype=torch.float32, pin_memory=True)
+    addr = _pinned_device_address(pool)
+    slots = np.random.default_rng(0).permutation(n + 32)[:n].astype(np.int64)
+    slots_d = torch.from_numpy(slots).to("cuda:0")
+    each = Hv * d * d * 4
+    fn = lambda: gdn.gdn_snapshot_copy(src, n, each, addr, slots_d, slots, n + 32, copy_stream=stream)
+    fn()
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(pool[torch.from_numpy(slots[:4])], src[:4].cpu()))
+    t_copy = statistics.median(Timer(torch, stream).run(fn, reps, flush))
+    init = torch.empty((32, Hv, d, d), dtype=torch.float32, device="cuda:0")
+    rs = torch.from_numpy(slots[:32])
+
+    def restore():
+        for i in range(32):
+            init[i].copy_(pool[int(rs[i])], non_blocking=True)
+    with torch.cuda.stream(stream):
+        restore()
+    torch.cuda.synchronize()
+    ok = ok and bool(torch.equal(init[:2].cpu(), pool[rs[:2]]))
+    with torch.cuda.stream(stream):
+        t_rest = statistics.median(Timer(torch, stream).run(restore, reps))
+    return {"workload": "prefix cache: 96 x 2 MiB checkpoints to a pinned host pool; 32 x 2 MiB restored",
+            "copy_ms": t_copy, "copy_GBs": n * each / (t_copy * 1e-3) / 1e9,
+            "restore_ms": t_rest, "restore_GBs": 32 * each / (t_rest * 1e-3) / 1e9, "exact": ok}
+
+
 def bench_decode(torch, gdn, stream, flush, reps):
     import workloads as W
     d = W.decode_batch(seed=0, batch=32, pool=64)
@@ -341,7 +385,8 @@ def main():
 
     legs = {}
     if not args.no_legs:
-        for name, f in (("conv", bench_conv), ("snapshot_copy", bench_snapshot), ("decode", bench_decode),
+        for name, f in (("conv", bench_conv), ("snapshot_copy", bench_snapshot),
+                        ("prefix_cache_host", bench_prefix_cache), ("decode", bench_decode),
                         ("mixed", bench_mixed)):
             log(f"[bench] leg {name}")
             legs[name] = f(torch, gdn, stream, flush, 10)
