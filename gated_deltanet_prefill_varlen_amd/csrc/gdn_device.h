@@ -133,4 +133,18 @@ __device__ __forceinline__ int seq_of_token(const int32_t* cu, int n_seqs, int p
   return lo;
 }
 
+// The same search for a block-uniform p, through the constant address space:
+// the compiler reads cu with scalar loads, which do not queue behind the
+// block's vector loads in flight.
+__device__ __forceinline__ int seq_of_token_uniform(const int32_t* cu_ptr, int n_seqs, int p) {
+  typedef const int32_t __attribute__((address_space(4)))* ConstI32;
+  const ConstI32 cu = (ConstI32)cu_ptr;
+  int lo = 0, hi = n_seqs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 }  // namespace gdn

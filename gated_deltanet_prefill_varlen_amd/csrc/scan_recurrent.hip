@@ -2,10 +2,12 @@
 // a state pool, and a token-by-token prefill used for the fp32 io path.
 //
 // Work split: one workgroup owns 32 rows (value dims) of one (sequence, value
-// head) state; each row is spread over DK/16 consecutive lanes holding 16
-// consecutive key dims in registers.  Row sums (S k, S q, |k|^2, |q|^2) are
-// lane-group reductions in a fixed order, so a row's arithmetic never depends
-// on which workgroup or launch computes it.
+// head) state; each row is spread over LPR = DK/16 consecutive lanes, lane
+// part j holding the four-element chunks at key dims 4 LPR i + 4 j (i = 0..3),
+// so the LPR lanes of a row read whole 64- to 128-byte segments per load
+// instruction.  Row sums (S k, S q, |k|^2, |q|^2) are lane-group reductions
+// in a fixed order, so a row's arithmetic never depends on which workgroup or
+// launch computes it.
 #include <climits>
 
 #include "gdn_device.h"
@@ -28,11 +30,11 @@ __device__ __forceinline__ float token_step(float* S, float* kv, float* qv, floa
     for (int i = 0; i < 16; ++i) { sk = fmaf(kv[i], kv[i], sk); sq = fmaf(qv[i], qv[i], sq); }
     sk = group_sum<LPR>(sk);
     sq = group_sum<LPR>(sq);
-    const float rk = 1.0f / sqrtf(sk + eps), rq = 1.0f / sqrtf(sq + eps);
+    const float rk = __builtin_amdgcn_rsqf(sk + eps), rq = __builtin_amdgcn_rsqf(sq + eps);
 #pragma unroll
     for (int i = 0; i < 16; ++i) { kv[i] *= rk; qv[i] *= rq; }
   }
-  const float alpha = expf(g);
+  const float alpha = __expf(g);
   float x = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) x = fmaf(S[i], kv[i], x);
@@ -47,6 +49,38 @@ __device__ __forceinline__ float token_step(float* S, float* kv, float* qv, floa
   return group_sum<LPR>(o);
 }
 
+// The lane's 16 elements of a row (chunks of four at 4 LPR i + 4 j).
+template <int LPR>
+__device__ __forceinline__ void load_row16f(const float* row, int j, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 x = *reinterpret_cast<const float4*>(row + 4 * LPR * i + 4 * j);
+    out[4 * i] = x.x; out[4 * i + 1] = x.y; out[4 * i + 2] = x.z; out[4 * i + 3] = x.w;
+  }
+}
+template <int LPR>
+__device__ __forceinline__ void store_row16f(float* row, int j, const float* v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<float4*>(row + 4 * LPR * i + 4 * j) =
+        make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+template <int LPR, typename IO>
+__device__ __forceinline__ void load_row16(const typename IO::T* row, int j, float* out) {
+  if constexpr (IO::kBytes == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 w = *reinterpret_cast<const uint2*>(row + 4 * LPR * i + 4 * j);
+      out[4 * i] = __uint_as_float(w.x << 16);
+      out[4 * i + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+      out[4 * i + 2] = __uint_as_float(w.y << 16);
+      out[4 * i + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+    }
+  } else {
+    load_row16f<LPR>(reinterpret_cast<const float*>(row), j, out);
+  }
+}
+
 template <int DK, int DV, typename IO>
 __global__ void __launch_bounds__(kRows * (DK / 16))
 recurrent_prefill_kernel(const ScanArgs a) {
@@ -55,14 +89,14 @@ recurrent_prefill_kernel(const ScanArgs a) {
   const int s = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int row = blockIdx.z * kRows + tid / LPR;
-  const int kb = (tid % LPR) * 16;
+  const int jl = tid % LPR;
   const int j = h / (a.Hv / a.Hqk);
   const int t0 = a.cu[s], t1 = a.cu[s + 1];
 
   float S[16];
-  const size_t head_off = ((size_t)h * DV + row) * DK + kb;
+  const size_t head_off = ((size_t)h * DV + row) * DK;
   const size_t state_stride = (size_t)a.Hv * DV * DK;
-  if (a.init) load16f(a.init + (size_t)s * state_stride + head_off, S);
+  if (a.init) load_row16f<LPR>(a.init + (size_t)s * state_stride + head_off, jl, S);
   else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) S[i] = 0.f;
@@ -76,21 +110,19 @@ recurrent_prefill_kernel(const ScanArgs a) {
   T* op = static_cast<T*>(a.out);
   for (int t = t0; t < t1; ++t) {
     float kv[16], qv[16];
-    load8<IO>(kp + (size_t)t * a.k_stride + j * DK + kb, kv);
-    load8<IO>(kp + (size_t)t * a.k_stride + j * DK + kb + 8, kv + 8);
-    load8<IO>(qp + (size_t)t * a.q_stride + j * DK + kb, qv);
-    load8<IO>(qp + (size_t)t * a.q_stride + j * DK + kb + 8, qv + 8);
+    load_row16<LPR, IO>(kp + (size_t)t * a.k_stride + j * DK, jl, kv);
+    load_row16<LPR, IO>(qp + (size_t)t * a.q_stride + j * DK, jl, qv);
     const float vrow = load1<IO>(vp + (size_t)t * a.v_stride + (size_t)h * DV + row);
     const float g = a.g[(size_t)t * a.Hv + h], beta = a.beta[(size_t)t * a.Hv + h];
     const float o = token_step<LPR>(S, kv, qv, vrow, g, beta, a.l2norm, a.eps);
-    if (tid % LPR == 0) store1<IO>(op + ((size_t)t * a.Hv + h) * DV + row, a.scale * o);
+    if (jl == 0) store1<IO>(op + ((size_t)t * a.Hv + h) * DV + row, a.scale * o);
     if (t + 1 == next) {
-      store16f(a.ckpt_buf + (size_t)ci * state_stride + head_off, S);
+      store_row16f<LPR>(a.ckpt_buf + (size_t)ci * state_stride + head_off, jl, S);
       ++ci;
       next = ci < a.n_ckpt ? a.ckpt[ci] : INT_MAX;
     }
   }
-  if (a.final_state) store16f(a.final_state + (size_t)s * state_stride + head_off, S);
+  if (a.final_state) store_row16f<LPR>(a.final_state + (size_t)s * state_stride + head_off, jl, S);
 }
 
 template <int DK, int DV, typename IO>
@@ -101,23 +133,19 @@ decode_kernel(const DecodeArgs a) {
   const int b = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int row = blockIdx.z * kRows + tid / LPR;
-  const int kb = (tid % LPR) * 16;
+  const int jl = tid % LPR;
   const int j = h / (a.Hv / a.Hqk);
   const int r = a.slot ? a.slot[b] : b;
-  float* sp = a.state + (((size_t)r * a.Hv + h) * DV + row) * DK + kb;
+  float* sp = a.state + (((size_t)r * a.Hv + h) * DV + row) * DK;
   float S[16], kv[16], qv[16];
-  load16f(sp, S);
-  const T* kp = static_cast<const T*>(a.k) + (size_t)b * a.k_stride + j * DK + kb;
-  const T* qp = static_cast<const T*>(a.q) + (size_t)b * a.q_stride + j * DK + kb;
-  load8<IO>(kp, kv);
-  load8<IO>(kp + 8, kv + 8);
-  load8<IO>(qp, qv);
-  load8<IO>(qp + 8, qv + 8);
+  load_row16f<LPR>(sp, jl, S);
+  load_row16<LPR, IO>(static_cast<const T*>(a.k) + (size_t)b * a.k_stride + j * DK, jl, kv);
+  load_row16<LPR, IO>(static_cast<const T*>(a.q) + (size_t)b * a.q_stride + j * DK, jl, qv);
   const float vrow = load1<IO>(static_cast<const T*>(a.v) + (size_t)b * a.v_stride + (size_t)h * DV + row);
   const float o = token_step<LPR>(S, kv, qv, vrow, a.g[(size_t)b * a.Hv + h],
                                   a.beta[(size_t)b * a.Hv + h], a.l2norm, a.eps);
-  store16f(sp, S);
-  if (tid % LPR == 0)
+  store_row16f<LPR>(sp, jl, S);
+  if (jl == 0)
     store1<IO>(static_cast<T*>(a.out) + ((size_t)b * a.Hv + h) * DV + row, a.scale * o);
 }
 
