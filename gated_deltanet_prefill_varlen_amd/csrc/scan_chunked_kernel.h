@@ -88,17 +88,25 @@ __device__ __forceinline__ void split_half(const f32x16& x, bf16x8& hi, bf16x8& 
   lo = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
 }
 
-// Sum of squares of the eight bf16 values in a 16-byte vector.
-__device__ __forceinline__ float sumsq8(const u32x4& w) {
-  float s = 0.f;
-  const uint32_t r[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float x0 = __uint_as_float(r[p] << 16), x1 = __uint_as_float(r[p] & 0xFFFF0000u);
-    s = fmaf(x0, x0, s);
-    s = fmaf(x1, x1, s);
+// Sum of squares of the four bf16 values in an 8-byte piece.
+__device__ __forceinline__ float sumsq4(const u32x2& w) {
+  const float x0 = __uint_as_float(w.x << 16), x1 = __uint_as_float(w.x & 0xFFFF0000u);
+  const float x2 = __uint_as_float(w.y << 16), x3 = __uint_as_float(w.y & 0xFFFF0000u);
+  return fmaf(x3, x3, fmaf(x2, x2, fmaf(x1, x1, x0 * x0)));
+}
+
+// Total over an aligned group of W lanes (8, 16 or 32), exact in the group's
+// last lane (for 32: the 16-lane sums, then the lower row's total added into
+// the upper row by row_bcast:15), in a fixed order.
+template <int W>
+__device__ __forceinline__ float lane_group_total(float x) {
+  if constexpr (W <= 16) {
+    return group_sum<W>(x);
+  } else {
+    x = group_sum<16>(x);
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142,
+                                                                      0xA, 0xF, false));
   }
-  return s;
 }
 
 // Inclusive prefix sum over lanes 0..31 (each 16-lane row by shifts of 1, 2,
@@ -175,9 +183,12 @@ struct Cfg {
   static_assert(oQ % 16 == 0 && oKt % 16 == 0 && oV % 16 == 0 && oT % 16 == 0 && oA % 16 == 0, "align");
   // the next chunk's rows wait in registers (16-byte vectors per thread)
   // while this chunk computes, when they fit in 32 registers
-  static constexpr int NVK = (CT * DK / 8 + NTH - 1) / NTH;
+  // K and Q come in cells of 4 tokens x 4 key dims (four 8-byte row pieces),
+  // V in 16-byte row pieces
+  static constexpr int KC = DK / 4;                    // cells across a row
+  static constexpr int NCK = (CT / 4 * KC + NTH - 1) / NTH;
   static constexpr int NVV = (CT * DV / 8 + NTH - 1) / NTH;
-  static constexpr bool PREFETCH = (2 * NVK + NVV) * 4 <= 32;
+  static constexpr bool PREFETCH = NCK * 16 + NVV * 4 <= 32;
 };
 
 // per-token scalar arrays (index into the scalar block)
@@ -254,11 +265,16 @@ chunked_prefill_kernel(const ScanArgs a) {
   // One chunk's HBM rows into registers.  Every lane loads (row index clamped
   // into the chunk, so no load is conditional); rows past the chunk's end are
   // zeroed where they are consumed.
-  auto ld_kq = [&](int u, int t0x, int nx, u32x4& kx, u32x4& qx) {
-    const int e = min(tid + u * NTH, CT * DK / 8 - 1);
-    const int t = min(e / (DK / 8), nx - 1), c8 = (e % (DK / 8)) * 8;
-    kx = *reinterpret_cast<const u32x4*>(kg + (size_t)(t0x + t) * a.k_stride + (size_t)j * DK + c8);
-    qx = *reinterpret_cast<const u32x4*>(qg + (size_t)(t0x + t) * a.q_stride + (size_t)j * DK + c8);
+  struct Cell { u32x2 k[4], q[4]; };   // rows 4 tg + r, key dims 4 kc .. 4 kc + 3
+  auto ld_kq = [&](int u, int t0x, int nx, Cell& x) {
+    const int e = min(tid + u * NTH, CT / 4 * C::KC - 1);
+    const int tg = e / C::KC, kc = e % C::KC;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = min(4 * tg + r, nx - 1);
+      x.k[r] = *reinterpret_cast<const u32x2*>(kg + (size_t)(t0x + t) * a.k_stride + (size_t)j * DK + 4 * kc);
+      x.q[r] = *reinterpret_cast<const u32x2*>(qg + (size_t)(t0x + t) * a.q_stride + (size_t)j * DK + 4 * kc);
+    }
   };
   auto ld_v = [&](int u, int t0x, int nx, u32x4& vx) {
     const int e = min(tid + u * NTH, CT * DV / 8 - 1);
@@ -272,12 +288,13 @@ chunked_prefill_kernel(const ScanArgs a) {
   };
   // with PREFETCH the rows of the next chunk are held here between chunks;
   // otherwise each vector is loaded where it is consumed
-  constexpr int NPK = C::PREFETCH ? C::NVK : 1, NPV = C::PREFETCH ? C::NVV : 1;
-  u32x4 pk[NPK], pq[NPK], pv[NPV];
+  constexpr int NPK = C::PREFETCH ? C::NCK : 1, NPV = C::PREFETCH ? C::NVV : 1;
+  Cell pkq[NPK];
+  u32x4 pv[NPV];
   float pg, pb;
   auto fetch = [&](int t0x, int nx) {
 #pragma unroll
-    for (int u = 0; u < NPK; ++u) ld_kq(u, t0x, nx, pk[u], pq[u]);
+    for (int u = 0; u < NPK; ++u) ld_kq(u, t0x, nx, pkq[u]);
 #pragma unroll
     for (int u = 0; u < NPV; ++u) ld_v(u, t0x, nx, pv[u]);
     ld_gb(t0x, nx, pg, pb);
@@ -360,34 +377,55 @@ chunked_prefill_kernel(const ScanArgs a) {
     //         registers before V lands, stored to HBM after.
     if constexpr (!C::PREFETCH) ld_gb(t0, n, pg, pb);
     {
-      constexpr int VPR = DK / 8;          // 16-byte vectors per row = lanes per row
-      static_assert((CT * DK / 8) % 64 == 0 && VPR <= 16, "row lanes");
+      // a cell: four 8-byte row pieces of K and of Q; K goes to LDS row-major
+      // and, transposed in registers, as four 8-byte pieces of four tokens.
+      // A token's squares are summed over its KC lanes (a fixed-order DPP sum
+      // ending in the group's last lane).
+      constexpr int KC = C::KC;
+      static_assert(KC == 8 || KC == 16 || KC == 32, "cell lanes");
+      static_assert(NTH % KC == 0, "cell rows");
 #pragma unroll
-      for (int u = 0; u < C::NVK; ++u) {
+      for (int u = 0; u < C::NCK; ++u) {
         const int e = tid + u * NTH;
-        if (e < CT * DK / 8) {             // whole waves per trip
-          const int t = e / VPR, c8 = (e % VPR) * 8;
-          u32x4 kx, qx;
-          if constexpr (C::PREFETCH) { kx = pk[u]; qx = pq[u]; } else ld_kq(u, t0, n, kx, qx);
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 kv = t < n ? kx : z, qv = t < n ? qx : z;
-          u32x2* kd = reinterpret_cast<u32x2*>(sK + t * LDK + c8);
-          u32x2* qd = reinterpret_cast<u32x2*>(sQ + t * LDK + c8);
-          kd[0] = u32x2{kv.x, kv.y}; kd[1] = u32x2{kv.z, kv.w};
-          qd[0] = u32x2{qv.x, qv.y}; qd[1] = u32x2{qv.z, qv.w};
-          const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+        if (e < CT / 4 * KC) {             // whole lane groups per trip
+          const int tg = e / KC, kc = e % KC;
+          Cell x;
+          if constexpr (C::PREFETCH) x = pkq[u]; else ld_kq(u, t0, n, x);
+          const u32x2 z = {0u, 0u};
+          float sk[4], sq[4];
 #pragma unroll
-          for (int p2 = 0; p2 < 4; ++p2) {
-            sKt[(c8 + 2 * p2) * LDKT + t] = (uint16_t)(kw[p2] & 0xFFFFu);
-            sKt[(c8 + 2 * p2 + 1) * LDKT + t] = (uint16_t)(kw[p2] >> 16);
+          for (int r = 0; r < 4; ++r) {
+            const int t = 4 * tg + r;
+            if (t >= n) { x.k[r] = z; x.q[r] = z; }
+            *reinterpret_cast<u32x2*>(sK + t * LDK + 4 * kc) = x.k[r];
+            *reinterpret_cast<u32x2*>(sQ + t * LDK + 4 * kc) = x.q[r];
+            sk[r] = sumsq4(x.k[r]);
+            sq[r] = sumsq4(x.q[r]);
           }
-          float sk = sumsq8(kv), sq = sumsq8(qv);
-          sk = group_sum<VPR>(sk);
-          sq = group_sum<VPR>(sq);
-          if (e % VPR == 0) {   // zero-padded rows past n keep r = 1 (no 0 * inf)
-            const bool nrm = a.l2norm && t < n;
-            sRk[t] = nrm ? __builtin_amdgcn_rsqf(sk + a.eps) : 1.0f;
-            sRq[t] = nrm ? __builtin_amdgcn_rsqf(sq + a.eps) : 1.0f;
+          // transposed: key dim 4 kc + d, tokens 4 tg .. 4 tg + 3
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int hw = d & 1;
+            auto part = [&](int r) { return d < 2 ? x.k[r].x : x.k[r].y; };
+            const uint32_t w0 = hw ? (part(0) >> 16) | (part(1) & 0xFFFF0000u)
+                                   : (part(0) & 0xFFFFu) | (part(1) << 16);
+            const uint32_t w1 = hw ? (part(2) >> 16) | (part(3) & 0xFFFF0000u)
+                                   : (part(2) & 0xFFFFu) | (part(3) << 16);
+            *reinterpret_cast<u32x2*>(sKt + (4 * kc + d) * LDKT + 4 * tg) = u32x2{w0, w1};
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sk[r] = lane_group_total<KC>(sk[r]);
+            sq[r] = lane_group_total<KC>(sq[r]);
+          }
+          if (kc == KC - 1) {   // zero-padded rows past n keep r = 1 (no 0 * inf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 4 * tg + r;
+              const bool nrm = a.l2norm && t < n;
+              sRk[t] = nrm ? __builtin_amdgcn_rsqf(sk[r] + a.eps) : 1.0f;
+              sRq[t] = nrm ? __builtin_amdgcn_rsqf(sq[r] + a.eps) : 1.0f;
+            }
           }
         }
       }
