@@ -588,6 +588,18 @@ chunked_prefill_kernel(const ScanArgs a) {
     // ---- 5. state path for this wave's 32 value columns
     if constexpr (!C::SPLIT) xqs(X, QS);
     {
+      // the LDS operands of the stage are requested ahead of their use, so the
+      // LDS round trips overlap: V of this wave's columns first, then the T
+      // and P row operands (hi and lo planes), the K^T row operands of the
+      // update (with several waves) once O is out
+      const uint16_t* tr = sT + c * LDT + 4 * g;
+      const uint16_t* pr = sP + c * LDT + 4 * g;
+      float vv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vv[i] = bf16_to_f32(sV[acc_row(i, g) * LDV + v]);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 tA[4] = {lds_op(tr), lds_op(tr + TPL), lds_op(tr + 16), lds_op(tr + TPL + 16)};
+
       // Y = beta (V - r_k e^G X), in place of X (zero past n)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -597,30 +609,27 @@ chunked_prefill_kernel(const ScanArgs a) {
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float vvv = bf16_to_f32(sV[(tb + r) * LDV + v]);
-          const float y = bb[r] * (vvv - kk[r] * X[4 * q4 + r]);
+          const float y = bb[r] * (vv[4 * q4 + r] - kk[r] * X[4 * q4 + r]);
           X[4 * q4 + r] = tb + r < n ? y : 0.f;
         }
       }
-      // product of a split 32x32 LDS block (rows at rowp) with a split tile
-      auto tri_mm = [&](const uint16_t* rowp, const uint16_t* lo_plane_rowp, const f32x16& y,
-                        f32x16 acc) {
+      const bf16x8 pA[4] = {lds_op(pr), lds_op(pr + TPL), lds_op(pr + 16), lds_op(pr + TPL + 16)};
+      // product of a split 32x32 LDS block (operands a: hi, lo of columns
+      // 0..15, then of 16..31) with a split tile
+      auto tri_mm = [&](const bf16x8 (&ao)[4], const f32x16& y, f32x16 acc) {
         bf16x8 yh0, yl0, yh1, yl1;
         split_half<0>(y, yh0, yl0);
         split_half<1>(y, yh1, yl1);
-        const bf16x8 a0h = lds_op(rowp), a0l = lds_op(lo_plane_rowp);
-        const bf16x8 a1h = lds_op(rowp + 16), a1l = lds_op(lo_plane_rowp + 16);
-        acc = mma(a0h, yh0, acc);
-        acc = mma(a0l, yh0, acc);
-        acc = mma(a0h, yl0, acc);
-        acc = mma(a1h, yh1, acc);
-        acc = mma(a1l, yh1, acc);
-        acc = mma(a1h, yl1, acc);
+        acc = mma(ao[0], yh0, acc);
+        acc = mma(ao[1], yh0, acc);
+        acc = mma(ao[0], yl0, acc);
+        acc = mma(ao[2], yh1, acc);
+        acc = mma(ao[3], yh1, acc);
+        acc = mma(ao[2], yl1, acc);
         return acc;
       };
       // U = T Y
-      const uint16_t* tr = sT + c * LDT + 4 * g;
-      f32x16 U = tri_mm(tr, tr + TPL, X, f32x16{});
+      f32x16 U = tri_mm(tA, X, f32x16{});
       // O = scale r_q e^G (Q S0^T) + P U, into this wave's own columns of the
       // V/O tile (V of these columns was consumed above by this wave only);
       // stored out next chunk
@@ -630,10 +639,14 @@ chunked_prefill_kernel(const ScanArgs a) {
         QS[4 * q4] *= c4.x; QS[4 * q4 + 1] *= c4.y;
         QS[4 * q4 + 2] *= c4.z; QS[4 * q4 + 3] *= c4.w;
       }
-      const uint16_t* pr = sP + c * LDT + 4 * g;
-      QS = tri_mm(pr, pr + TPL, U, QS);
+      QS = tri_mm(pA, U, QS);
 #pragma unroll
       for (int i = 0; i < 16; ++i) sV[acc_row(i, g) * LDV + v] = bf16_bits(QS[i]);
+      bf16x8 kta[NKS];
+      auto ldt = [&](int kt, int h2) { return lds_op(sKt + (32 * kt + c) * LDKT + 16 * h2 + 4 * g); };
+      if constexpr (PRE)
+#pragma unroll
+        for (int ks = 0; ks < DK / 16; ++ks) kta[ks] = ldt(ks / 2, ks % 2);
       // S = e^{G_C} S + K^T (r_k e^{G_C - G} U); K^T rows from the transposed tile
       const float gC = __expf(sG[CT - 1]);
 #pragma unroll
@@ -649,11 +662,6 @@ chunked_prefill_kernel(const ScanArgs a) {
       bf16x8 uh[2], ul[2];
       split_half<0>(U, uh[0], ul[0]);
       split_half<1>(U, uh[1], ul[1]);
-      bf16x8 kta[NKS];
-      auto ldt = [&](int kt, int h2) { return lds_op(sKt + (32 * kt + c) * LDKT + 16 * h2 + 4 * g); };
-      if constexpr (PRE)
-#pragma unroll
-        for (int ks = 0; ks < DK / 16; ++ks) kta[ks] = ldt(ks / 2, ks % 2);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
