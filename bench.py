@@ -298,6 +298,81 @@ def bench_mixed(torch, gdn, stream, flush, reps):
             "ms_median": med, "tokens_per_s": toks / (med * 1e-3)}
 
 
+def bench_overlap(torch, gdn, stream, flush, reps):
+    """Work on its own streams overlapping: (a) the mixed pass, prefill pack on
+    one stream and the decode batch on another, against each alone; (b) the
+    checkpoint copy of one layer on a copy stream while the next layer's scan
+    runs, against the same launches serialised on one stream (device pool,
+    and pinned host pool over the host link)."""
+    import workloads as W
+    sA, sB = stream, torch.cuda.Stream()
+
+    def joined(fa, fb, b_first=False):
+        """fa on sA and fb on sB from a common start (fb enqueued first when
+        b_first), sA waiting for sB at the end."""
+        def run():
+            e0 = torch.cuda.Event()
+            e0.record(sA)
+            sB.wait_event(e0)
+            if b_first:
+                fb()
+                fa()
+            else:
+                fa()
+                fb()
+            e1 = torch.cuda.Event()
+            e1.record(sB)
+            sA.wait_event(e1)
+        return run
+
+    med = lambda fn, st: statistics.median(Timer(torch, st).run(fn, reps, flush))
+    out = {}
+    # (a) mixed pass
+    pack, d = W.mixed_step(seed=0)
+    dp = DevPack(torch, gdn, pack, [])
+    q, k, v = (io_t(torch, a, "bf16") for a in (d.q, d.k, d.v))
+    g, b = f32_t(torch, d.g), f32_t(torch, d.beta)
+    st, slot = f32_t(torch, d.state), i32_t(torch, d.slot)
+    o = torch.empty((32, 32, 128), dtype=torch.bfloat16, device="cuda:0")
+    shape = gdn.make_shape(16, 32, 128, 128, 64)
+    pre = lambda: dp.run(stream=sA)
+    dec_a = lambda: gdn.gdn_decode_step(shape, q, k, v, g, b, st, slot, d.slot, o, stream=sA)
+    dec_b = lambda: gdn.gdn_decode_step(shape, q, k, v, g, b, st, slot, d.slot, o, stream=sB)
+    t_p, t_d = med(pre, sA), med(dec_a, sA)
+    t_serial = med(lambda: (pre(), dec_a()), sA)
+    t_two = med(joined(pre, dec_b), sA)
+    out["mixed_pass"] = {"prefill_ms": t_p, "decode_ms": t_d, "one_stream_ms": t_serial,
+                         "two_streams_ms": t_two, "overlap_saved_ms": t_serial - t_two}
+    del dp
+    # (b) checkpoint copy beside the next layer's scan
+    p = W.chat_wave(seed=0)
+    ck = gdn.gdn_plan_checkpoints(p.cu_seqlens, p.block)
+    l1, l2 = DevPack(torch, gdn, p, ck), DevPack(torch, gdn, p, ck)
+    n, each = len(ck), p.Hv * p.dv * p.dk * 4
+    slots = np.random.default_rng(0).permutation(n + 32)[:n].astype(np.int64)
+    slots_d = torch.from_numpy(slots).to("cuda:0")
+    dev_pool = torch.empty((n + 32, p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
+    host_pool = torch.empty((n + 32, p.Hv, p.dv, p.dk), dtype=torch.float32, pin_memory=True)
+    host_addr = _pinned_device_address(host_pool)
+    for name, dst in (("device_pool", dev_pool), ("host_pool", host_addr)):
+        copy_a = lambda: gdn.gdn_snapshot_copy(l1.ckbuf, n, each, dst, slots_d, slots, n + 32,
+                                               copy_stream=sA)
+        copy_b = lambda: gdn.gdn_snapshot_copy(l1.ckbuf, n, each, dst, slots_d, slots, n + 32,
+                                               copy_stream=sB)
+        scan1, scan2 = (lambda: l1.run(stream=sA)), (lambda: l2.run(stream=sA))
+        t_copy = med(copy_a, sA)
+        t_serial = med(lambda: (scan1(), copy_a(), scan2()), sA)
+
+        def overlapped():   # as an engine would: the copy enqueued before the next scan
+            scan1()
+            joined(scan2, copy_b, b_first=True)()
+        t_two = med(overlapped, sA)
+        out[f"copy_beside_next_scan_{name}"] = {"copy_ms": t_copy, "one_stream_ms": t_serial,
+                                                "copy_stream_ms": t_two, "overlap_saved_ms": t_serial - t_two}
+    del l1, l2
+    return out
+
+
 # ------------------------------------------------------------ CPU oracle --
 
 def _oracle_one_prompt(args):
@@ -352,6 +427,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-prompts", type=int, default=32)
     ap.add_argument("--workload", default="chat", choices=["chat", "long", "ragged"])
+    ap.add_argument("--overlap-only", action="store_true",
+                    help="run only the stream-overlap leg (for a rocprofv3 timeline)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on exactly one GPU (the path shards by value-head groups "
@@ -371,6 +448,9 @@ def main():
     makers = {"chat": (W.chat_wave, "chat wave 32 x 1,024 tokens"),
               "long": (W.long_prompts, "long prompts 4 x 8,192 tokens"),
               "ragged": (W.ragged_pack, "ragged 8 prompts <= 8,192 tokens, prefix-cache init")}
+    if args.overlap_only:
+        print(json.dumps({"overlap": bench_overlap(torch, gdn, stream, flush, 10)}), flush=True)
+        return
     fn, label = makers[args.workload]
     log(f"[bench] generating {label}")
     p = fn(seed=0)
@@ -387,7 +467,7 @@ def main():
     if not args.no_legs:
         for name, f in (("conv", bench_conv), ("snapshot_copy", bench_snapshot),
                         ("prefix_cache_host", bench_prefix_cache), ("decode", bench_decode),
-                        ("mixed", bench_mixed)):
+                        ("mixed", bench_mixed), ("overlap", bench_overlap)):
             log(f"[bench] leg {name}")
             legs[name] = f(torch, gdn, stream, flush, 10)
         for wname in ("long", "ragged"):

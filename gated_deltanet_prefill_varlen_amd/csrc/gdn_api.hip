@@ -288,7 +288,14 @@ gdn_status gdn_snapshot_copy(const void* ckpt_buf, int32_t n, int64_t bytes_each
   if (wait_event) e = hipStreamWaitEvent(s, reinterpret_cast<hipEvent_t>(wait_event), 0);
   if (e != hipSuccess) return GDN_ERR_HIP;
   if (n > 0) {
-    gdn::CopyArgs a{ckpt_buf, n, bytes_each, dst_pool, dst_slot};
+    // A pool in host memory is bounded by the host link: the gather then runs
+    // on one workgroup per item, which keeps the link saturated (faster here
+    // than one DMA transfer per item) while holding few CUs.
+    hipPointerAttribute_t attr{};
+    const hipError_t pe = hipPointerGetAttributes(&attr, dst_pool);
+    if (pe != hipSuccess) (void)hipGetLastError();   // not a HIP allocation: treat as device
+    const int32_t host_dst = pe == hipSuccess && attr.type == hipMemoryTypeHost;
+    gdn::CopyArgs a{ckpt_buf, n, bytes_each, dst_pool, dst_slot, host_dst};
     const gdn_status r = finish_launch(gdn::launch_snapshot_copy(a, s), s);
     if (r != GDN_OK) return r;
   }

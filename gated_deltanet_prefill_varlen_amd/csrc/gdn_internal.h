@@ -70,6 +70,7 @@ struct CopyArgs {
   int64_t bytes_each;
   void* dst;
   const int64_t* slot;
+  int32_t host_dst;        // dst is host memory: one workgroup per item
 };
 
 hipError_t launch_prefill(const ScanArgs& a, hipStream_t stream);

@@ -1,7 +1,10 @@
 // Checkpoint copy: gathers checkpoint states into caller-owned pool slots
 // (device memory or device-mapped pinned host memory).  Pure streaming copy in
 // 16-byte vectors with non-temporal hints, so it does not evict the scan's
-// working set from the caches it shares while both run.
+// working set from the caches it shares while both run.  Into host memory one
+// workgroup per item keeps the host link saturated on few CUs (a copy there
+// runs about 8x longer than a chat-wave scan, and stalls the scan
+// workgroups that share its CUs).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -40,7 +43,7 @@ __global__ void __launch_bounds__(kThreads) snapshot_copy_kernel(const CopyArgs 
 hipError_t launch_snapshot_copy(const CopyArgs& a, hipStream_t st) {
   const int64_t n16 = a.bytes_each / 16;
   const int64_t per_block = (int64_t)kThreads * kPerThread;
-  const int gx = (int)std::min<int64_t>((n16 + per_block - 1) / per_block, 1024);
+  const int gx = a.host_dst ? 1 : (int)std::min<int64_t>((n16 + per_block - 1) / per_block, 1024);
   for (int i0 = 0; i0 < a.n; i0 += 65535) {
     CopyArgs b = a;
     b.src = static_cast<const char*>(a.src) + (size_t)i0 * a.bytes_each;

@@ -202,7 +202,10 @@ GDN_API gdn_status gdn_decode_step(const gdn_shape* shape, int32_t batch, const 
  *   ckpt_buf:      device memory, n * bytes_each bytes.
  *   bytes_each:    > 0 and a multiple of 16; both pointers 16-byte aligned.
  *   dst_pool:      device memory or device-mapped pinned host memory (e.g.
- *                  from hipHostMalloc), pool_slots * bytes_each bytes.
+ *                  from hipHostMalloc), pool_slots * bytes_each bytes.  Into
+ *                  host memory (hipPointerGetAttributes) the gather runs on
+ *                  one workgroup per item: the host link bounds it, so few
+ *                  CUs are held while it runs.
  *   dst_slot:      device int64 [n]; dst_slot_host its host mirror, each in
  *                  [0, pool_slots) and all distinct.
  *   wait_event, done_event: hipEvent_t as void*, or NULL.
