@@ -235,6 +235,35 @@ def decode_step(q, k, v, g, beta, state, slot=None, scale: float = 1.0,
     return out, new_state
 
 
+def decode_tokens(q, k, v, g, beta, state, n_tok: int, slot=None, scale: float = 1.0,
+                  l2norm: bool = True, eps: float = DEFAULT_EPS):
+    """n_tok recurrent steps for each of B sequences on state[slot[b]], with
+    the state after every token kept (speculative or multi-token-prediction
+    verification, rolled back by restoring a kept state).
+
+    q, k: [B * n_tok, Hqk, dk]; v: [B * n_tok, Hv, dv]; g, beta: [B * n_tok,
+    Hv], sequence-major (row b * n_tok + i).  Returns (out [B * n_tok, Hv, dv],
+    new_state, snapshots [B, n_tok, Hv, dv, dk]) with snapshot i the state
+    after token i + 1 and the addressed pool rows at the state after the last
+    token.  Defined as a prefill of each sequence's n_tok tokens from its slot
+    state with a checkpoint after every token.
+    """
+    B = q.shape[0] // n_tok
+    slot = np.arange(B) if slot is None else np.asarray(slot)
+    new_state = np.array(state, dtype=np.float64)
+    cu = np.arange(B + 1) * n_tok
+    marks = [int(cu[b] + i) for b in range(B) for i in range(1, n_tok + 1) if i < n_tok]
+    out, fin, ck = prefill_recurrent(q, k, v, g, beta, cu, init=new_state[slot], ckpt_positions=marks,
+                                     scale=scale, l2norm=l2norm, eps=eps)
+    Hv, dv, dk = fin.shape[1:]
+    snaps = np.zeros((B, n_tok, Hv, dv, dk))
+    if n_tok > 1:
+        snaps[:, :n_tok - 1] = ck.reshape(B, n_tok - 1, Hv, dv, dk)
+    snaps[:, n_tok - 1] = fin
+    new_state[slot] = fin
+    return out, new_state, snaps
+
+
 # ---------------------------------------------------------- chunked oracle --
 
 def prefill_chunked(q, k, v, g, beta, cu_seqlens, chunk, init=None, ckpt_positions=(),
@@ -311,6 +340,6 @@ def max_rel_rows(x: np.ndarray, ref: np.ndarray) -> np.ndarray:
 
 __all__ = [
     "DEFAULT_EPS", "bf16_to_f64", "to_f64", "round_bf16", "l2_rnorm", "plan_checkpoints",
-    "conv1d_silu_packed", "prefill_recurrent", "prefill_chunked", "decode_step",
+    "conv1d_silu_packed", "prefill_recurrent", "prefill_chunked", "decode_step", "decode_tokens",
     "rel_frobenius", "max_rel_rows",
 ]

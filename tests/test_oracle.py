@@ -229,6 +229,31 @@ def test_decode_is_one_token_step_on_addressed_slots():
         np.testing.assert_array_equal(new[slot[b]], f1[0])
 
 
+def test_decode_tokens_is_successive_decode_steps():
+    """n tokens at once, with the state after each kept, equal n one-token
+    steps (up to fp64 rounding order), and the last kept state is the final."""
+    rng = np.random.default_rng(15)
+    B, n, P = 3, 4, 6
+    q = rng.standard_normal((B * n, 2, 8)); k = rng.standard_normal((B * n, 2, 8))
+    v = rng.standard_normal((B * n, 4, 6)); g = -rng.random((B * n, 4)); beta = rng.random((B * n, 4))
+    state = rng.standard_normal((P, 4, 6, 8))
+    slot = np.array([5, 1, 3])
+    out, new, snaps = O.decode_tokens(q, k, v, g, beta, state, n, slot, scale=0.7)
+    cur = np.array(state)
+    for i in range(n):
+        rows = np.arange(B) * n + i
+        o1, cur = O.decode_step(q[rows], k[rows], v[rows], g[rows], beta[rows], cur, slot, scale=0.7)
+        np.testing.assert_allclose(out[rows], o1, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(snaps[:, i], cur[slot], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(new, cur, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(snaps[:, -1], new[slot])
+    np.testing.assert_array_equal(new[[0, 2, 4]], state[[0, 2, 4]])
+    o1, s1, sn1 = O.decode_tokens(q[::n], k[::n], v[::n], g[::n], beta[::n], state, 1, slot, scale=0.7)
+    o2, s2 = O.decode_step(q[::n], k[::n], v[::n], g[::n], beta[::n], state, slot, scale=0.7)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
 # -------------------------------------------------------------- planner ----
 
 def _golden_planner():
