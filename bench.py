@@ -277,6 +277,30 @@ def bench_decode(torch, gdn, stream, flush, reps):
             "achieved_GBs": B / (med * 1e-3) / 1e9, "roofline_frac": B / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_decode_tokens(torch, gdn, stream, flush, reps):
+    """Speculative verification: 32 sequences x 4 tokens, the state after each
+    token kept (snapshots), pool rows advanced by 4 tokens."""
+    import workloads as W
+    B, n = 32, 4
+    ds = [W.decode_batch(seed=10 + i, batch=B) for i in range(n)]
+    cat = lambda key: np.stack([getattr(d, key) for d in ds], axis=1).reshape((B * n,) + getattr(ds[0], key).shape[1:])
+    q, k, v = (io_t(torch, cat(a), "bf16") for a in ("q", "k", "v"))
+    g, b = f32_t(torch, cat("g")), f32_t(torch, cat("beta"))
+    st, slot = f32_t(torch, ds[0].state), i32_t(torch, ds[0].slot)
+    out = torch.empty((B * n, 32, 128), dtype=torch.bfloat16, device="cuda:0")
+    snaps = torch.empty((B, n, 32, 128, 128), dtype=torch.float32, device="cuda:0")
+    shape = gdn.make_shape(16, 32, 128, 128, 64)
+    fn = lambda: gdn.gdn_decode_tokens(shape, n, q, k, v, g, b, st, slot, ds[0].slot, out, snaps, stream=stream)
+    fn()
+    times = Timer(torch, stream).run(fn, reps, flush)
+    med = statistics.median(times)
+    each = 32 * 128 * 128 * 4
+    B_alg = B * each * (2 + n) + B * n * (2 * 16 * 128 * 2 + 32 * 128 * 2 * 2 + 32 * 8)
+    return {"workload": "decode 32 seqs x 4 tokens x 32 heads, state kept after every token",
+            "ms_median": med, "achieved_GBs": B_alg / (med * 1e-3) / 1e9,
+            "roofline_frac": B_alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def bench_mixed(torch, gdn, stream, flush, reps):
     import workloads as W
     pack, d = W.mixed_step(seed=0)
@@ -467,6 +491,7 @@ def main():
     if not args.no_legs:
         for name, f in (("conv", bench_conv), ("snapshot_copy", bench_snapshot),
                         ("prefix_cache_host", bench_prefix_cache), ("decode", bench_decode),
+                        ("decode_tokens", bench_decode_tokens),
                         ("mixed", bench_mixed), ("overlap", bench_overlap)):
             log(f"[bench] leg {name}")
             legs[name] = f(torch, gdn, stream, flush, 10)

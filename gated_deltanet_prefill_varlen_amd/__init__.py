@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "GdnError", "gdn_shape", "make_shape", "load", "GDN_BF16", "GDN_F32", "GDN_QK_L2NORM",
     "gdn_status_string", "gdn_plan_checkpoints", "gdn_prefill_packed", "gdn_decode_step",
+    "gdn_decode_tokens",
     "gdn_conv1d_silu_packed", "gdn_snapshot_copy", "LIB_PATH", "EXPORTED",
 ]
 
@@ -32,7 +33,7 @@ GDN_QK_L2NORM = 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_SEQLENS", 5: "GDN_ERR_CKPT", 6: "GDN_ERR_CAPACITY", 7: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_status_string", "gdn_plan_checkpoints", "gdn_conv1d_silu_packed",
-            "gdn_prefill_packed", "gdn_decode_step", "gdn_snapshot_copy")
+            "gdn_prefill_packed", "gdn_decode_step", "gdn_decode_tokens", "gdn_snapshot_copy")
 
 
 class GdnError(RuntimeError):
@@ -84,6 +85,8 @@ def load() -> ctypes.CDLL:
                                        _P, _P, _I32, _P, _P, _P, _P]
     lib.gdn_decode_step.restype = _I32
     lib.gdn_decode_step.argtypes = [_SP, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P]
+    lib.gdn_decode_tokens.restype = _I32
+    lib.gdn_decode_tokens.argtypes = [_SP, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P]
     lib.gdn_conv1d_silu_packed.restype = _I32
     lib.gdn_conv1d_silu_packed.argtypes = [_SP, _P, _P, _I32, _I32, _P, _I64, _P, _P, _P, _I64,
                                            _P, _P, _P, _I32, _P, _P]
@@ -191,6 +194,17 @@ def gdn_decode_step(shape: gdn_shape, q, k, v, g, beta, state, slot=None, slot_h
         ctypes.byref(shape), int(q.shape[0]), _dev(q), _dev(k), _dev(v), _dev(g), _dev(beta),
         _dev(state), int(state.shape[0]), _dev(slot), _hp(sl_h), _dev(out), _stream(stream)),
         "gdn_decode_step")
+
+
+def gdn_decode_tokens(shape: gdn_shape, n_tok: int, q, k, v, g, beta, state, slot=None,
+                      slot_host=None, out=None, snapshots=None, stream=None) -> None:
+    """n_tok tokens per sequence (rows b * n_tok + i), states kept per token."""
+    sl_h = _host_i32(slot_host)
+    batch = int(q.shape[0]) // int(n_tok)
+    _check(load().gdn_decode_tokens(
+        ctypes.byref(shape), batch, int(n_tok), _dev(q), _dev(k), _dev(v), _dev(g), _dev(beta),
+        _dev(state), int(state.shape[0]), _dev(slot), _hp(sl_h), _dev(out), _dev(snapshots),
+        _stream(stream)), "gdn_decode_tokens")
 
 
 def gdn_conv1d_silu_packed(shape: gdn_shape, cu_seqlens, cu_seqlens_host, x, weight, y,

@@ -180,9 +180,18 @@ gdn_status gdn_decode_step(const gdn_shape* shape, int32_t batch, const void* q,
                            const void* v, const float* g, const float* beta, float* state,
                            int64_t pool_slots, const int32_t* slot, const int32_t* slot_host,
                            void* out, void* stream) {
+  return gdn_decode_tokens(shape, batch, 1, q, k, v, g, beta, state, pool_slots, slot, slot_host, out,
+                           nullptr, stream);
+}
+
+gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t batch, int32_t n_tok, const void* q,
+                             const void* k, const void* v, const float* g, const float* beta,
+                             float* state, int64_t pool_slots, const int32_t* slot,
+                             const int32_t* slot_host, void* out, float* snapshots, void* stream) {
   gdn_status st = check_shape(shape);
   if (st != GDN_OK) return st;
-  if (batch < 0 || pool_slots < 0) return GDN_ERR_SHAPE;
+  if (batch < 0 || pool_slots < 0 || n_tok < 1) return GDN_ERR_SHAPE;
+  if ((int64_t)batch * n_tok > INT32_MAX) return GDN_ERR_SHAPE;
   if (batch == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_NULL;
   if (slot) {
@@ -202,12 +211,13 @@ gdn_status gdn_decode_step(const gdn_shape* shape, int32_t batch, const void* q,
   if ((st = resolve_stride(shape, shape->q_tok_stride, Hqk * dk, &qs)) != GDN_OK) return st;
   if ((st = resolve_stride(shape, shape->k_tok_stride, Hqk * dk, &ks)) != GDN_OK) return st;
   if ((st = resolve_stride(shape, shape->v_tok_stride, Hv * dv, &vs)) != GDN_OK) return st;
-  const void* ptrs[] = {q, k, v, out, state};
+  const void* ptrs[] = {q, k, v, out, state, snapshots};
   for (const void* p : ptrs)
-    if (!aligned16(p)) return GDN_ERR_SHAPE;
+    if (p && !aligned16(p)) return GDN_ERR_SHAPE;
 
   gdn::DecodeArgs a{};
-  a.batch = batch; a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.batch = batch; a.n_tok = n_tok; a.snap = snapshots;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.state = state; a.slot = slot; a.out = out;
   a.q_stride = qs; a.k_stride = ks; a.v_stride = vs;
   a.Hqk = (int32_t)Hqk; a.Hv = (int32_t)Hv; a.dk = (int32_t)dk; a.dv = (int32_t)dv;

@@ -31,6 +31,8 @@ struct ScanArgs {
 
 struct DecodeArgs {
   int32_t batch;
+  int32_t n_tok;           // tokens per sequence (rows b * n_tok + i)
+  float* snap;             // [batch, n_tok, Hv, dv, dk] or nullptr
   const void* q;
   const void* k;
   const void* v;

@@ -137,16 +137,22 @@ decode_kernel(const DecodeArgs a) {
   const int j = h / (a.Hv / a.Hqk);
   const int r = a.slot ? a.slot[b] : b;
   float* sp = a.state + (((size_t)r * a.Hv + h) * DV + row) * DK;
-  float S[16], kv[16], qv[16];
+  float S[16];
   load_row16f<LPR>(sp, jl, S);
-  load_row16<LPR, IO>(static_cast<const T*>(a.k) + (size_t)b * a.k_stride + j * DK, jl, kv);
-  load_row16<LPR, IO>(static_cast<const T*>(a.q) + (size_t)b * a.q_stride + j * DK, jl, qv);
-  const float vrow = load1<IO>(static_cast<const T*>(a.v) + (size_t)b * a.v_stride + (size_t)h * DV + row);
-  const float o = token_step<LPR>(S, kv, qv, vrow, a.g[(size_t)b * a.Hv + h],
-                                  a.beta[(size_t)b * a.Hv + h], a.l2norm, a.eps);
+  // the sequence's tokens in order, the state staying in registers; the
+  // state after each token to its snapshot when asked for
+  for (int i = 0; i < a.n_tok; ++i) {
+    const size_t t = (size_t)b * a.n_tok + i;
+    float kv[16], qv[16];
+    load_row16<LPR, IO>(static_cast<const T*>(a.k) + t * a.k_stride + j * DK, jl, kv);
+    load_row16<LPR, IO>(static_cast<const T*>(a.q) + t * a.q_stride + j * DK, jl, qv);
+    const float vrow = load1<IO>(static_cast<const T*>(a.v) + t * a.v_stride + (size_t)h * DV + row);
+    const float o = token_step<LPR>(S, kv, qv, vrow, a.g[t * a.Hv + h], a.beta[t * a.Hv + h],
+                                    a.l2norm, a.eps);
+    if (jl == 0) store1<IO>(static_cast<T*>(a.out) + (t * a.Hv + h) * DV + row, a.scale * o);
+    if (a.snap) store_row16f<LPR>(a.snap + ((t * a.Hv + h) * DV + row) * DK, jl, S);
+  }
   store_row16f<LPR>(sp, jl, S);
-  if (jl == 0)
-    store1<IO>(static_cast<T*>(a.out) + ((size_t)b * a.Hv + h) * DV + row, a.scale * o);
 }
 
 template <int DK, int DV, typename IO>

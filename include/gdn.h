@@ -191,6 +191,30 @@ GDN_API gdn_status gdn_decode_step(const gdn_shape* shape, int32_t batch, const 
                            int64_t pool_slots, const int32_t* slot, const int32_t* slot_host,
                            void* out, void* stream);
 
+/* n_tok recurrent steps for each of `batch` decoding sequences, in place on
+ * the state pool, keeping the state after every token: the verification pass
+ * of speculative or multi-token-prediction decoding, where a rejected suffix
+ * is rolled back by restoring a kept state (sparkinfer README, supported
+ * speculation: draft-model and multi-token prediction; Qwen3-Next uses
+ * multi-token prediction).  gdn_decode_step is the n_tok = 1 case.
+ *   n_tok:      tokens per sequence, >= 1.
+ *   q, k:       device io_dtype [batch * n_tok, Hqk, dk], sequence-major (row
+ *               b * n_tok + i is token i of sequence b; token stride from
+ *               shape);  v: [batch * n_tok, Hv, dv];
+ *   g, beta:    device fp32 [batch * n_tok, Hv].
+ *   state:      device fp32 [pool_slots, Hv, dv, dk]; the addressed rows end
+ *               at the state after the sequence's last token.
+ *   slot, slot_host, pool_slots: as in gdn_decode_step.
+ *   out:        device io_dtype [batch * n_tok, Hv, dv].
+ *   snapshots:  device fp32 [batch, n_tok, Hv, dv, dk] (entry i: the state
+ *               after token i of the sequence), or NULL.
+ * The arithmetic per token is gdn_decode_step's, so n_tok calls of it give
+ * the same bits.  Errors: as gdn_decode_step (n_tok < 1: GDN_ERR_SHAPE). */
+GDN_API gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t batch, int32_t n_tok, const void* q,
+                             const void* k, const void* v, const float* g, const float* beta,
+                             float* state, int64_t pool_slots, const int32_t* slot,
+                             const int32_t* slot_host, void* out, float* snapshots, void* stream);
+
 /* Checkpoint copy on its own stream (sparkinfer release v0.6.28: the scan and
  * the checkpoint copy of checkpointing prompts run on their own streams, and
  * pinned host buffers for checkpoints are allocated when the prefix cache

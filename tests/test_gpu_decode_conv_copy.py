@@ -42,6 +42,60 @@ def test_decode_step_vs_oracle(dtype, pool):
     assert np.max(O.max_rel_rows(to_f64(out), ro)) <= OUT_TOL[dtype]
 
 
+def _token_rows(a, n_tok, batch):
+    """Rows of a [batch, ...] array drawn per token: [batch * n_tok, ...]."""
+    return a.reshape((batch * n_tok,) + a.shape[2:]) if a.ndim > 1 else a
+
+
+def test_decode_tokens_vs_oracle_and_successive_steps():
+    """Speculative verification: 4 tokens per sequence with the state after
+    each kept.  Against the oracle (tolerance) and bitwise against 4 calls of
+    gdn_decode_step (same per-token arithmetic)."""
+    B, n, Hqk, Hv, d = 16, 4, 4, 8, 128
+    rng = np.random.default_rng(21)
+    P = 24
+    q = W.f32_to_bf16_bits(_unit(rng.standard_normal((B * n, Hqk, d))))
+    k = W.f32_to_bf16_bits(_unit(rng.standard_normal((B * n, Hqk, d))))
+    v = W.f32_to_bf16_bits(rng.standard_normal((B * n, Hv, d)))
+    g = (-np.log1p(np.exp(rng.standard_normal((B * n, Hv))))).astype(np.float32)
+    beta = (1 / (1 + np.exp(-rng.standard_normal((B * n, Hv))))).astype(np.float32)
+    state = (0.1 * rng.standard_normal((P, Hv, d, d))).astype(np.float32)
+    slot = rng.permutation(P)[:B].astype(np.int32)
+    shape = gdn.make_shape(Hqk, Hv, d, d, 64)
+    st = f32_tensor(state)
+    out = torch.empty((B * n, Hv, d), dtype=torch.bfloat16, device=DEV)
+    snaps = torch.empty((B, n, Hv, d, d), dtype=torch.float32, device=DEV)
+    gdn.gdn_decode_tokens(shape, n, io_tensor(q, "bf16"), io_tensor(k, "bf16"), io_tensor(v, "bf16"),
+                          f32_tensor(g), f32_tensor(beta), st, i32_tensor(slot), slot, out, snaps)
+    # the same tokens as n one-token steps
+    st2 = f32_tensor(state)
+    outs = []
+    for i in range(n):
+        rows = np.arange(B) * n + i
+        o = torch.empty((B, Hv, d), dtype=torch.bfloat16, device=DEV)
+        gdn.gdn_decode_step(shape, io_tensor(q[rows], "bf16"), io_tensor(k[rows], "bf16"),
+                            io_tensor(v[rows], "bf16"), f32_tensor(g[rows]), f32_tensor(beta[rows]), st2,
+                            i32_tensor(slot), slot, o)
+        torch.cuda.synchronize()
+        outs.append(o)
+        assert torch.equal(snaps[:, i], st2[torch.from_numpy(slot).long().to(DEV)])
+    torch.cuda.synchronize()
+    assert torch.equal(st, st2)
+    for i in range(n):
+        assert torch.equal(out[torch.from_numpy(np.arange(B) * n + i).to(DEV)], outs[i])
+    ro, rs, rsn = O.decode_tokens(O.to_f64(q, "bf16"), O.to_f64(k, "bf16"), O.to_f64(v, "bf16"),
+                                  g.astype(np.float64), beta.astype(np.float64), state.astype(np.float64),
+                                  n, slot)
+    assert np.max(O.max_rel_rows(to_f64(out), ro)) <= OUT_TOL["bf16"]
+    assert np.max(O.rel_frobenius(to_f64(st)[slot], rs[slot])) <= STATE_TOL
+    assert np.max(O.rel_frobenius(to_f64(snaps).reshape(B * n, Hv, d, d),
+                                  rsn.reshape(B * n, Hv, d, d))) <= STATE_TOL
+
+
+def _unit(x):
+    return (x / np.linalg.norm(x, axis=-1, keepdims=True)).astype(np.float32)
+
+
 def test_decode_identity_slots_and_small_heads():
     d = W.decode_batch(seed=4, batch=5, Hqk=2, Hv=4, dk=32, dv=64)
     q, k, v, g, b, st, _, out = _decode_dev(d)
