@@ -153,3 +153,39 @@ def test_slow_decay_ragged_init_visible():
     dp = DevPack(p, _ckpt(p)).run()
     torch.cuda.synchronize()
     assert_parity(dp, sample_pairs(p, 12, seed=3))
+
+
+def _degenerate_pack(case):
+    """A small ragged pack with one of the method's degenerate inputs."""
+    p = W.make_pack(case, [130, 64, 33], 2, 4, 128, 128, 64, 64, seed=31, init_std=0.1)
+    T = p.n_tokens
+    if case == "beta0_g0":            # no write and no decay: the state is carried unchanged
+        p.beta[:] = 0.0
+        p.g[:] = 0.0
+    elif case == "no_decay":          # g = 0: pure delta rule, nothing forgets
+        p.g[:] = 0.0
+    elif case == "beta1_repeated_keys":   # beta = 1, runs of 8 tokens with one key: overwrites
+        p.beta[:] = 1.0
+        for t in range(T):
+            p.k[t] = p.k[t - t % 8]
+    elif case == "strong_decay":      # e^G underflows inside a chunk
+        p.g[:] = -30.0
+    elif case == "zero_rows":         # all-zero k, q or v rows (the L2 norm gives zero vectors)
+        p.k[::5] = 0
+        p.q[::3] = 0
+        p.v[::7] = 0
+    else:
+        raise ValueError(case)
+    return p
+
+
+@pytest.mark.parametrize("case", ["beta0_g0", "no_decay", "beta1_repeated_keys", "strong_decay",
+                                  "zero_rows"])
+def test_degenerate_inputs(case):
+    p = _degenerate_pack(case)
+    dp = DevPack(p, _ckpt(p)).run()
+    torch.cuda.synchronize()
+    if case == "beta0_g0":
+        np.testing.assert_array_equal(to_f64(dp.final), p.init.astype(np.float64))
+    eo, es = assert_parity(dp, all_pairs(p))
+    print(f"{case}: out {eo:.2e} state {es:.2e}")
