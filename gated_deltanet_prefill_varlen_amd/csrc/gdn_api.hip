@@ -31,11 +31,12 @@ gdn_status check_shape(const gdn_shape* s) {
 
 int64_t elem_bytes(const gdn_shape* s) { return s->io_dtype == GDN_BF16 ? 2 : 4; }
 
-// Resolve a token stride (0 = dense) and check that it fits the row and keeps
-// 16-byte alignment of every row.
+// Resolve a token stride (0 = dense) and check that it fits the row, stays
+// below 2^23 elements (the kernels address the rows of a chunk with 32-bit
+// offsets) and keeps 16-byte alignment of every row.
 gdn_status resolve_stride(const gdn_shape* s, int64_t given, int64_t dense, int64_t* out) {
   const int64_t st = given == 0 ? dense : given;
-  if (st < dense) return GDN_ERR_SHAPE;
+  if (st < dense || st >= (int64_t(1) << 23)) return GDN_ERR_SHAPE;
   if ((st * elem_bytes(s)) % 16 != 0) return GDN_ERR_SHAPE;
   *out = st;
   return GDN_OK;

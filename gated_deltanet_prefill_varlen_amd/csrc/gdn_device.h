@@ -92,9 +92,13 @@ __device__ __forceinline__ void store16f(float* p, const float* v) {
 
 // ------------------------------------------------------- lane reductions --
 // Lane exchange inside a row of 16 lanes (DPP, no LDS round trip).
+// x read from another lane of its row by DPP control CTRL.  Only in-row
+// permutations are used (every source lane exists), so the bound_ctrl bit,
+// set here so that the compiler folds the move into the consuming add,
+// changes no value.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over aligned groups of W consecutive lanes (W a power of two <= 16):

@@ -11,25 +11,25 @@
 // (Yang et al., "Parallelizing Linear Transformers with the Delta Rule over
 // Sequence Length", NeurIPS 2024, UT transform; gated as in Gated Delta
 // Networks, ICLR 2025.)  The L2 norms enter only as fp32 row scalings, so the
-// raw bf16 q/k/v are exact MFMA operands.
+// raw q/k rows are exact MFMA operands.
 //
 // Work split (DV/32 waves): all waves stage K and Q of the chunk in LDS and
-// share the Gram / Q K^T tiles and the inversion of the 32x32 diagonal blocks
-// of (I + A) (forward substitution, several lanes per column); the
-// off-diagonal block is applied to Y directly, U1 = T11 Y1,
-// U2 = T22 (Y2 - A21 U1), so T21 is never formed.  Wave w owns state columns
-// v in [32w, 32w+32): its slice of S stays in MFMA accumulator registers for
-// the whole prompt (fp32), laid out as S^T tiles (rows k, lane column v).
-// LDS is kept under 80 KB and registers under 256 so two workgroups share a
-// CU and overlap each other's latency-bound phases.
+// share the Gram / Q K^T tiles and the inversion of the 32x32 diagonal block
+// of (I + A) (forward substitution, several lanes per column).  Wave w owns
+// state columns v in [32w, 32w+32): its slice of S stays in MFMA accumulator
+// registers for the whole prompt (fp32), laid out as S^T tiles (rows k, lane
+// column v).  LDS is kept under 80 KB and registers under 256 so two
+// workgroups share a CU and overlap each other's latency-bound phases.
 //
-// Precision: every product that carries fp32 values uses split bf16 operands
-// (x = hi + lo, hi = bf16(x), lo = bf16(x - hi); the lo*lo pass dropped):
-// K S0^T and Q S0^T with S0 split (2 passes), T Y, A21 U1, P U with both
-// sides split (3 passes), K^T U' with U' split (2 passes).  A dot of a unit q
-// with a state row is ~1/sqrt(dk) of |q||S row| while single bf16 rounding
-// errors are not, which is why the output products are split too.
-// Accumulation is fp32 throughout.
+// Precision: every product runs on fp16 operands with fp32 accumulation.
+// The raw bf16 q/k rows convert to fp16 exactly (fp16 carries three more
+// significand bits; values must lie inside fp16's range, |x| < 65504, and
+// rows keep full accuracy while their norm is at least 2^-10).  Values the
+// kernel computes in fp32 (S0, T, P, Y, U) are rounded to fp16 once per
+// product (2^-11 relative), which holds states to about 4e-4 relative
+// Frobenius against fp64 over thousands of tokens, with or without decay;
+// the state itself is accumulated and carried in fp32.  S must also stay
+// inside fp16's range.
 #pragma once
 
 #include <climits>
@@ -41,58 +41,54 @@
 namespace gdn {
 namespace chunked {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// D(32x32) += A(32x16) B(16x32).  Lane l: A row l%32 and B column l%32, with
-// eight k values each; D register i holds row 8(i/4) + 4(l/32) + i%4,
-// column l%32.
-__device__ __forceinline__ f32x16 mma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// D(32x32) += A(32x16) B(16x32) on fp16 operands.  Lane l: A row l%32 and B
+// column l%32, with eight k values each; D register i holds row
+// 8(i/4) + 4(l/32) + i%4, column l%32.
+__device__ __forceinline__ f32x16 mma(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// MFMA operand from a bf16 row in LDS.  The k order used by every product:
+// MFMA operand from an fp16 row in LDS.  The k order used by every product:
 // within a 16-wide k step at offset 16*h2, lane half g (= l/32) holds
 // k = 16*h2 + 4g + {0,1,2,3} and 16*h2 + 8 + 4g + {0,1,2,3}; this is exactly
 // the row order of accumulator registers 8*h2 .. 8*h2+7, so an accumulator
 // tile feeds the next product as its B operand without moving data.
 // `p` points at element 16*h2 + 4g of the row (8-byte aligned).
-__device__ __forceinline__ bf16x8 lds_op(const uint16_t* p) {
+__device__ __forceinline__ f16x8 lds_op(const uint16_t* p) {
   const u32x2 a = *reinterpret_cast<const u32x2*>(p);
   const u32x2 b = *reinterpret_cast<const u32x2*>(p + 8);
   const u32x4 v = {a.x, a.y, b.x, b.y};
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(f16x8, v);
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Two fp32 values as packed bf16 hi terms and packed bf16 lo terms
-// (hi = bf16(x), lo = bf16(x - hi)), two values per conversion.
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
-  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xFFFF0000u);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
+// Two fp32 values as packed fp16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, f16x2));
 }
 
-// Accumulator half h2 (registers 8h2..8h2+7) as a B operand, split into
-// hi + lo bf16 terms.
+// Accumulator half h2 (registers 8h2..8h2+7) as a B operand.
 template <int H2>
-__device__ __forceinline__ void split_half(const f32x16& x, bf16x8& hi, bf16x8& lo) {
-  uint32_t hw[4], lw[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) split2(x[8 * H2 + 2 * p], x[8 * H2 + 2 * p + 1], hw[p], lw[p]);
-  hi = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
-  lo = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+__device__ __forceinline__ f16x8 acc_half(const f32x16& x) {
+  const u32x4 w = {pack_f16(x[8 * H2], x[8 * H2 + 1]), pack_f16(x[8 * H2 + 2], x[8 * H2 + 3]),
+                   pack_f16(x[8 * H2 + 4], x[8 * H2 + 5]), pack_f16(x[8 * H2 + 6], x[8 * H2 + 7])};
+  return __builtin_bit_cast(f16x8, w);
 }
 
-// Sum of squares of the four bf16 values in an 8-byte piece.
-__device__ __forceinline__ float sumsq4(const u32x2& w) {
+// Four bf16 values (an 8-byte row piece) as four fp16 values, exact inside
+// fp16's range; ss gets their sum of squares.
+__device__ __forceinline__ u32x2 bf16x4_to_f16(const u32x2& w, float& ss) {
   const float x0 = __uint_as_float(w.x << 16), x1 = __uint_as_float(w.x & 0xFFFF0000u);
   const float x2 = __uint_as_float(w.y << 16), x3 = __uint_as_float(w.y & 0xFFFF0000u);
-  return fmaf(x3, x3, fmaf(x2, x2, fmaf(x1, x1, x0 * x0)));
+  ss = fmaf(x3, x3, fmaf(x2, x2, fmaf(x1, x1, x0 * x0)));
+  return u32x2{pack_f16(x0, x1), pack_f16(x2, x3)};
 }
 
 // Total over an aligned group of W lanes (8, 16 or 32), exact in the group's
@@ -138,11 +134,7 @@ __device__ __forceinline__ float group_bcast(float x) {
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-__device__ __forceinline__ void store_split(uint16_t* hi_plane, int plane_stride, int idx, float x) {
-  const __bf16 h = (__bf16)x;
-  hi_plane[idx] = __builtin_bit_cast(uint16_t, h);
-  hi_plane[plane_stride + idx] = bf16_bits(x - (float)h);
-}
+__device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 // Row of accumulator register i for lane half g.
 __device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
@@ -153,9 +145,9 @@ struct Cfg {
   static constexpr int NW = DV / 32;      // waves
   static constexpr int NTH = 64 * NW;     // threads
   static constexpr int KT = DK / 32;      // 32-wide k tiles of the state
-  static constexpr int LDK = DK + 4;      // row stride of sK, sQ (bf16; 8-byte aligned rows)
-  static constexpr int LDKT = CT + 4;     // row stride of sKt, the transposed K tile (bf16)
-  static constexpr int LDT = CT + 4;      // row stride of sT, sP (bf16)
+  static constexpr int LDK = DK + 4;      // row stride of sK, sQ (fp16; 8-byte aligned rows)
+  static constexpr int LDKT = CT + 4;     // row stride of sKt, the transposed K tile (fp16)
+  static constexpr int LDT = CT + 4;      // row stride of sT, sP (fp16)
   static constexpr int LDV = DV + 8;      // row stride of the V / O tile (bf16; 16-byte rows)
   static constexpr int LDA = CT + 4;      // row stride of sA, A transposed (fp32)
   // With four waves, waves 2 and 3 run the substitution while waves 0 and 1
@@ -172,9 +164,9 @@ struct Cfg {
   static constexpr int oQ = oK + CT * LDK * 2;
   static constexpr int oKt = oQ + CT * LDK * 2;
   static constexpr int oV = oKt + DK * LDKT * 2;      // V tile, then the O tile
-  static constexpr int oT = oV + CT * LDV * 2;        // hi then lo plane
-  static constexpr int oP = oT + 2 * CT * LDT * 2;    // hi then lo plane
-  static constexpr int oA = oP + 2 * CT * LDT * 2;
+  static constexpr int oT = oV + CT * LDV * 2;
+  static constexpr int oP = oT + CT * LDT * 2;
+  static constexpr int oA = oP + CT * LDT * 2;
   static constexpr int oS = oA + CT * LDA * 4;        // per-token scalars
   static constexpr int kScal = 8;
   static constexpr int bytes = oS + kScal * CT * 4;
@@ -216,7 +208,6 @@ chunked_prefill_kernel(const ScanArgs a) {
   float* sCk = sc + SC_CK * CT;     // r_k e^G
   float* sCq = sc + SC_CQ * CT;     // scale r_q e^G
   float* sCu = sc + SC_CU * CT;     // r_k e^{G_C - G}
-  constexpr int TPL = CT * LDT;     // bf16 elements per hi/lo plane
 
   const int s = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -265,26 +256,34 @@ chunked_prefill_kernel(const ScanArgs a) {
   // One chunk's HBM rows into registers.  Every lane loads (row index clamped
   // into the chunk, so no load is conditional); rows past the chunk's end are
   // zeroed where they are consumed.
+  // A row address is a workgroup-uniform base at the chunk's first token
+  // plus a 32-bit byte offset per lane: token strides are below 2^23
+  // elements, so the offsets of a chunk's rows come from 24-bit multiplies.
+  const uint32_t ksb = (uint32_t)a.k_stride * 2, qsb = (uint32_t)a.q_stride * 2;
+  const uint32_t vsb = (uint32_t)a.v_stride * 2, hv = (uint32_t)a.Hv;
+  auto row = [](const void* base, uint32_t off) { return static_cast<const char*>(base) + off; };
   struct Cell { u32x2 k[4], q[4]; };   // rows 4 tg + r, key dims 4 kc .. 4 kc + 3
   auto ld_kq = [&](int u, int t0x, int nx, Cell& x) {
     const int e = min(tid + u * NTH, CT / 4 * C::KC - 1);
     const int tg = e / C::KC, kc = e % C::KC;
+    const uint16_t* kb = kg + (size_t)t0x * a.k_stride + (size_t)j * DK;
+    const uint16_t* qb = qg + (size_t)t0x * a.q_stride + (size_t)j * DK;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = min(4 * tg + r, nx - 1);
-      x.k[r] = *reinterpret_cast<const u32x2*>(kg + (size_t)(t0x + t) * a.k_stride + (size_t)j * DK + 4 * kc);
-      x.q[r] = *reinterpret_cast<const u32x2*>(qg + (size_t)(t0x + t) * a.q_stride + (size_t)j * DK + 4 * kc);
+      const uint32_t t = min(4 * tg + r, nx - 1);
+      x.k[r] = *reinterpret_cast<const u32x2*>(row(kb, __umul24(t, ksb) + 8 * kc));
+      x.q[r] = *reinterpret_cast<const u32x2*>(row(qb, __umul24(t, qsb) + 8 * kc));
     }
   };
   auto ld_v = [&](int u, int t0x, int nx, u32x4& vx) {
     const int e = min(tid + u * NTH, CT * DV / 8 - 1);
-    const int t = min(e / (DV / 8), nx - 1), c8 = (e % (DV / 8)) * 8;
-    vx = *reinterpret_cast<const u32x4*>(vg + (size_t)(t0x + t) * a.v_stride + c8);
+    const uint32_t t = min(e / (DV / 8), nx - 1), c8 = (e % (DV / 8)) * 8;
+    vx = *reinterpret_cast<const u32x4*>(row(vg + (size_t)t0x * a.v_stride, __umul24(t, vsb) + 2 * c8));
   };
   auto ld_gb = [&](int t0x, int nx, float& gx, float& bx) {
-    const int tl = min(lane, nx - 1);
-    gx = a.g[(size_t)(t0x + tl) * a.Hv + h];
-    bx = a.beta[(size_t)(t0x + tl) * a.Hv + h];
+    const uint32_t tl = min(lane, nx - 1);
+    gx = a.g[(size_t)t0x * a.Hv + h + __umul24(tl, hv)];
+    bx = a.beta[(size_t)t0x * a.Hv + h + __umul24(tl, hv)];
   };
   // with PREFETCH the rows of the next chunk are held here between chunks;
   // otherwise each vector is loaded where it is consumed
@@ -312,11 +311,11 @@ chunked_prefill_kernel(const ScanArgs a) {
   constexpr bool PRE = C::NW > 1;
   constexpr int NKS = PRE ? DK / 16 : 1;
 
-  // X = K S0^T and QS = Q S0^T for this wave's columns, S0 split per k tile
-  // on the fly
+  // X = K S0^T and QS = Q S0^T for this wave's columns, S0 rounded to fp16
+  // per k tile on the fly
   auto xqs = [&](f32x16& X, f32x16& QS) {
-    bf16x8 ka[NKS], qa[NKS];
-    auto ld = [&](int ks, bf16x8& kx, bf16x8& qx) {
+    f16x8 ka[NKS], qa[NKS];
+    auto ld = [&](int ks, f16x8& kx, f16x8& qx) {
       const int off = c * LDK + 4 * g + 16 * ks;
       kx = lds_op(sK + off);
       qx = lds_op(sQ + off);
@@ -332,21 +331,18 @@ chunked_prefill_kernel(const ScanArgs a) {
       for (int h2 = 0; h2 < 2; ++h2) {
         const int ks = 2 * kt + h2;
         if constexpr (!PRE) ld(ks, ka[0], qa[0]);
-        const bf16x8& kx = ka[PRE ? ks : 0];
-        const bf16x8& qx = qa[PRE ? ks : 0];
-        bf16x8 sh, sl;
-        if (h2 == 0) split_half<0>(S[kt], sh, sl); else split_half<1>(S[kt], sh, sl);
+        const f16x8& kx = ka[PRE ? ks : 0];
+        const f16x8& qx = qa[PRE ? ks : 0];
+        const f16x8 sh = h2 == 0 ? acc_half<0>(S[kt]) : acc_half<1>(S[kt]);
         X = mma(kx, sh, X);
-        X = mma(kx, sl, X);
         QS = mma(qx, sh, QS);
-        QS = mma(qx, sl, QS);
       }
   };
 
   // Gram-type tile: sum over k of (row c of xa) (row c of xb), the A operand
   // rows giving the accumulator rows and the B operand rows its columns
   auto rows_mm = [&](const uint16_t* xa, const uint16_t* xb) {
-    bf16x8 ar[NKS], br[NKS];
+    f16x8 ar[NKS], br[NKS];
     if constexpr (PRE)
 #pragma unroll
       for (int ks = 0; ks < DK / 16; ++ks) {
@@ -369,16 +365,17 @@ chunked_prefill_kernel(const ScanArgs a) {
   for (int t0 = seq0; t0 < seq1; t0 += a.chunk) {
     const int n = min(a.chunk, seq1 - t0);   // valid rows of this chunk
 
-    // ---- 1. stage K (row-major and transposed) and Q rows (zero past n)
-    //         with their L2 norms (squares summed in registers, then over
+    // ---- 1. stage K (row-major and transposed) and Q rows as fp16 (zero past
+    //         n) with their L2 norms (squares summed in registers, then over
     //         the row's lanes), V rows, betas and the gate cumsum.  The rows
     //         were fetched into registers while the previous chunk ran.  The
     //         previous chunk's O rows leave the V/O tile first: read into
     //         registers before V lands, stored to HBM after.
     if constexpr (!C::PREFETCH) ld_gb(t0, n, pg, pb);
     {
-      // a cell: four 8-byte row pieces of K and of Q; K goes to LDS row-major
-      // and, transposed in registers, as four 8-byte pieces of four tokens.
+      // a cell: four 8-byte row pieces of K and of Q, converted to fp16; K
+      // goes to LDS row-major and, transposed in registers, as four 8-byte
+      // pieces of four tokens.
       // A token's squares are summed over its KC lanes (a fixed-order DPP sum
       // ending in the group's last lane).
       constexpr int KC = C::KC;
@@ -397,10 +394,10 @@ chunked_prefill_kernel(const ScanArgs a) {
           for (int r = 0; r < 4; ++r) {
             const int t = 4 * tg + r;
             if (t >= n) { x.k[r] = z; x.q[r] = z; }
+            x.k[r] = bf16x4_to_f16(x.k[r], sk[r]);
+            x.q[r] = bf16x4_to_f16(x.q[r], sq[r]);
             *reinterpret_cast<u32x2*>(sK + t * LDK + 4 * kc) = x.k[r];
             *reinterpret_cast<u32x2*>(sQ + t * LDK + 4 * kc) = x.q[r];
-            sk[r] = sumsq4(x.k[r]);
-            sq[r] = sumsq4(x.q[r]);
           }
           // transposed: key dim 4 kc + d, tokens 4 tg .. 4 tg + 3
 #pragma unroll
@@ -455,9 +452,10 @@ chunked_prefill_kernel(const ScanArgs a) {
 #pragma unroll
       for (int u = 0; u < C::NVV; ++u) {
         const int e = tid + u * NTH;
-        const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-        if (e < CT * DV / 8 && t < pn)
-          *reinterpret_cast<u32x4*>(og + (size_t)(pt0 + t) * a.Hv * DV + c8) = ov[u];
+        const uint32_t t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+        if (e < CT * DV / 8 && (int)t < pn)
+          *reinterpret_cast<u32x4*>(const_cast<char*>(row(og + (size_t)pt0 * a.Hv * DV,
+                                                          __umul24(t, hv * (2 * DV)) + 2 * c8))) = ov[u];
       }
     }
     __syncthreads();
@@ -501,8 +499,8 @@ chunked_prefill_kernel(const ScanArgs a) {
     if (wave == (C::NW > 1 ? 1 : 0)) {
       // K Q^T: A operand = K rows (accumulator row = key i), B operand = Q
       // rows (lane column = query t = c); P[t][i] = scale r_q,t r_k,i
-      // e^{G_t - G_i} q_t.k_i for i <= t, written as row t of P (hi and lo
-      // planes), four keys per 8-byte store
+      // e^{G_t - G_i} q_t.k_i for i <= t, written as row t of P (fp16), four
+      // keys per 8-byte store
       const f32x16 acc = rows_mm(sK, sQ);
       const float gt = sG[c], rt = a.scale * sRq[c];
 #pragma unroll
@@ -518,11 +516,8 @@ chunked_prefill_kernel(const ScanArgs a) {
           const float f = rt * Ri[r] * __expf(on ? gt - Gi[r] : 0.f) * acc[4 * q4 + r];
           pv4[r] = on ? f : 0.f;
         }
-        uint32_t h01, l01, h23, l23;
-        split2(pv4[0], pv4[1], h01, l01);
-        split2(pv4[2], pv4[3], h23, l23);
-        *reinterpret_cast<u32x2*>(sP + c * LDT + ib) = u32x2{h01, h23};
-        *reinterpret_cast<u32x2*>(sP + TPL + c * LDT + ib) = u32x2{l01, l23};
+        *reinterpret_cast<u32x2*>(sP + c * LDT + ib) =
+            u32x2{pack_f16(pv4[0], pv4[1]), pack_f16(pv4[2], pv4[3])};
       }
     }
     if constexpr (C::SPLIT)
@@ -579,7 +574,7 @@ chunked_prefill_kernel(const ScanArgs a) {
       }
       uint16_t* tcol = sT + jj;
 #pragma unroll
-      for (int m = 0; m < MPL; ++m) store_split(tcol, TPL, (q + LPC * m) * LDT, Tl[m]);
+      for (int m = 0; m < MPL; ++m) tcol[(q + LPC * m) * LDT] = f16_bits(Tl[m]);
     }
     if constexpr (C::SPLIT)
       if (wave < 2) xqs(X, QS);
@@ -590,17 +585,19 @@ chunked_prefill_kernel(const ScanArgs a) {
     {
       // the LDS operands of the stage are requested ahead of their use, so the
       // LDS round trips overlap: V of this wave's columns first, then the T
-      // and P row operands (hi and lo planes), the K^T row operands of the
-      // update (with several waves) once O is out
+      // and P row operands, the K^T row operands of the update (with several
+      // waves) once O is out
       const uint16_t* tr = sT + c * LDT + 4 * g;
       const uint16_t* pr = sP + c * LDT + 4 * g;
       float vv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) vv[i] = bf16_to_f32(sV[acc_row(i, g) * LDV + v]);
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 tA[4] = {lds_op(tr), lds_op(tr + TPL), lds_op(tr + 16), lds_op(tr + TPL + 16)};
+      const f16x8 tA[2] = {lds_op(tr), lds_op(tr + 16)};
 
-      // Y = beta (V - r_k e^G X), in place of X (zero past n)
+      // Y = beta (V - r_k e^G X), in place of X.  Rows past n come out as
+      // exact zeros: beta is 0 there, their V and K rows are zero (so X is)
+      // and r_k e^G is finite.
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int tb = 8 * q4 + 4 * g;
@@ -608,24 +605,14 @@ chunked_prefill_kernel(const ScanArgs a) {
         const float4 k4 = *reinterpret_cast<const float4*>(sCk + tb);
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float y = bb[r] * (vv[4 * q4 + r] - kk[r] * X[4 * q4 + r]);
-          X[4 * q4 + r] = tb + r < n ? y : 0.f;
-        }
+        for (int r = 0; r < 4; ++r) X[4 * q4 + r] = bb[r] * (vv[4 * q4 + r] - kk[r] * X[4 * q4 + r]);
       }
-      const bf16x8 pA[4] = {lds_op(pr), lds_op(pr + TPL), lds_op(pr + 16), lds_op(pr + TPL + 16)};
-      // product of a split 32x32 LDS block (operands a: hi, lo of columns
-      // 0..15, then of 16..31) with a split tile
-      auto tri_mm = [&](const bf16x8 (&ao)[4], const f32x16& y, f32x16 acc) {
-        bf16x8 yh0, yl0, yh1, yl1;
-        split_half<0>(y, yh0, yl0);
-        split_half<1>(y, yh1, yl1);
-        acc = mma(ao[0], yh0, acc);
-        acc = mma(ao[1], yh0, acc);
-        acc = mma(ao[0], yl0, acc);
-        acc = mma(ao[2], yh1, acc);
-        acc = mma(ao[3], yh1, acc);
-        acc = mma(ao[2], yl1, acc);
+      const f16x8 pA[2] = {lds_op(pr), lds_op(pr + 16)};
+      // product of a 32x32 LDS block (operands a: columns 0..15, then
+      // 16..31) with an accumulator tile
+      auto tri_mm = [&](const f16x8 (&ao)[2], const f32x16& y, f32x16 acc) {
+        acc = mma(ao[0], acc_half<0>(y), acc);
+        acc = mma(ao[1], acc_half<1>(y), acc);
         return acc;
       };
       // U = T Y
@@ -642,7 +629,7 @@ chunked_prefill_kernel(const ScanArgs a) {
       QS = tri_mm(pA, U, QS);
 #pragma unroll
       for (int i = 0; i < 16; ++i) sV[acc_row(i, g) * LDV + v] = bf16_bits(QS[i]);
-      bf16x8 kta[NKS];
+      f16x8 kta[NKS];
       auto ldt = [&](int kt, int h2) { return lds_op(sKt + (32 * kt + c) * LDKT + 16 * h2 + 4 * g); };
       if constexpr (PRE)
 #pragma unroll
@@ -659,17 +646,14 @@ chunked_prefill_kernel(const ScanArgs a) {
         U[4 * q4] *= c4.x; U[4 * q4 + 1] *= c4.y;
         U[4 * q4 + 2] *= c4.z; U[4 * q4 + 3] *= c4.w;
       }
-      bf16x8 uh[2], ul[2];
-      split_half<0>(U, uh[0], ul[0]);
-      split_half<1>(U, uh[1], ul[1]);
+      const f16x8 uh[2] = {acc_half<0>(U), acc_half<1>(U)};
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           if constexpr (!PRE) kta[0] = ldt(kt, h2);
-          const bf16x8& kx = kta[PRE ? 2 * kt + h2 : 0];
+          const f16x8& kx = kta[PRE ? 2 * kt + h2 : 0];
           S[kt] = mma(kx, uh[h2], S[kt]);
-          S[kt] = mma(kx, ul[h2], S[kt]);
         }
     }
     if (t0 + n == next_ck) {

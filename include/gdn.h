@@ -75,7 +75,9 @@ typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
  *   l2_eps:                    added to sum x^2 before the square root.
  *   q/k/v_tok_stride:          elements between consecutive tokens of q, k, v
  *                              (0 = dense: Hqk*dk, Hqk*dk, Hv*dv), so q, k and
- *                              v may be column views of one [T, conv_dim] row. */
+ *                              v may be column views of one [T, conv_dim] row;
+ *                              every token stride (given or dense, also x/y
+ *                              of the conv) is below 2^23 elements. */
 typedef struct gdn_shape {
   int32_t num_qk_heads;
   int32_t num_v_heads;
