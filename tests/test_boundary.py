@@ -109,6 +109,7 @@ def test_prefill_validation_errors():
     assert _prefill_call(out=FAKE + 4) == 2         # misaligned
     assert _prefill_call(S(q_tok_stride=32)) == 2   # shorter than one token row
     assert _prefill_call(S(k_tok_stride=65)) == 2   # rows not 16-byte aligned
+    assert _prefill_call(S(v_tok_stride=1 << 23)) == 2   # past the 32-bit row offsets
 
 
 def test_empty_pack_is_ok_without_any_launch():
