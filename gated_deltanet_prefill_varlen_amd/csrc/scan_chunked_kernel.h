@@ -91,6 +91,10 @@ __device__ __forceinline__ u32x2 bf16x4_to_f16(const u32x2& w, float& ss) {
   return u32x2{pack_f16(x0, x1), pack_f16(x2, x3)};
 }
 
+// 2^x on the hardware exp2 (v_exp_f32, about 1 ulp); decays are kept in
+// base 2 so that none needs a multiply first.
+__device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Total over an aligned group of W lanes (8, 16 or 32), exact in the group's
 // last lane (for 32: the 16-lane sums, then the lower row's total added into
 // the upper row by row_bcast:15), in a fixed order.
@@ -201,7 +205,7 @@ chunked_prefill_kernel(const ScanArgs a) {
   uint16_t* sP = reinterpret_cast<uint16_t*>(smem + C::oP);
   float* sA = reinterpret_cast<float*>(smem + C::oA);
   float* sc = reinterpret_cast<float*>(smem + C::oS);
-  float* sG = sc + SC_G * CT;       // cumsum of the log-gates
+  float* sG = sc + SC_G * CT;       // cumsum of the log-gates, times log2(e)
   float* sBeta = sc + SC_BETA * CT;
   float* sRk = sc + SC_RK * CT;
   float* sRq = sc + SC_RQ * CT;
@@ -390,10 +394,13 @@ chunked_prefill_kernel(const ScanArgs a) {
           if constexpr (C::PREFETCH) x = pkq[u]; else ld_kq(u, t0, n, x);
           const u32x2 z = {0u, 0u};
           float sk[4], sq[4];
+          if (n < CT)   // a prompt's last chunk (uniform branch): rows past n are zeros
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (4 * tg + r >= n) { x.k[r] = z; x.q[r] = z; }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = 4 * tg + r;
-            if (t >= n) { x.k[r] = z; x.q[r] = z; }
             x.k[r] = bf16x4_to_f16(x.k[r], sk[r]);
             x.q[r] = bf16x4_to_f16(x.q[r], sq[r]);
             *reinterpret_cast<u32x2*>(sK + t * LDK + 4 * kc) = x.k[r];
@@ -439,11 +446,13 @@ chunked_prefill_kernel(const ScanArgs a) {
           u32x4 vx;
           if constexpr (C::PREFETCH) vx = pv[u]; else ld_v(u, t0, n, vx);
           ov[u] = *seg;
-          *seg = t < n ? vx : u32x4{0u, 0u, 0u, 0u};
+          if (n < CT && t >= n) vx = u32x4{0u, 0u, 0u, 0u};
+          *seg = vx;
         }
       }
-      if (wave == 0) {  // betas and the inclusive scan of the log-gates (fixed order)
-        const float x = scan32(lane < n ? pg : 0.f);
+      if (wave == 0) {  // betas and the inclusive scan of the log-gates (fixed order),
+                        // kept in base 2 so every decay is one v_exp_f32
+        const float x = scan32(lane < n ? pg : 0.f) * 1.44269504088896341f;
         if (lane < CT) {
           sG[lane] = x;
           sBeta[lane] = lane < n ? pb : 0.f;
@@ -470,7 +479,9 @@ chunked_prefill_kernel(const ScanArgs a) {
       // Gram K K^T: both operands are the K rows (lane column = key i = c,
       // accumulator rows = token t); A[t][i] = beta_t r_t r_i e^{G_t - G_i} k_t.k_i
       // for i < t, stored transposed with rows interleaved over the LPC lane
-      // parts of the substitution: (t, i) at i*LDA + (t % LPC)*MPL + t / LPC
+      // parts of the substitution, each part's rows in descending order:
+      // (t, i) at i*LDA + (t % LPC)*MPL + MPL - 1 - t / LPC.  The rows a
+      // substitution step still needs are then an aligned prefix of the part.
       const f32x16 acc = rows_mm(sK, sK);
       const float gi = sG[c], ri = sRk[c];
 #pragma unroll
@@ -485,15 +496,15 @@ chunked_prefill_kernel(const ScanArgs a) {
         for (int r = 0; r < 4; ++r) {
           const int t = tb + r;
           const bool on = c < t;
-          const float f = Br[r] * Rr[r] * ri * __expf(on ? Gr[r] - gi : 0.f) * acc[4 * q4 + r];
-          sA[c * LDA + (t % LPC) * MPL + t / LPC] = on ? f : 0.f;
+          const float f = Br[r] * Rr[r] * ri * exp2f_hw(on ? Gr[r] - gi : 0.f) * acc[4 * q4 + r];
+          sA[c * LDA + (t % LPC) * MPL + MPL - 1 - t / LPC] = on ? f : 0.f;
         }
       }
       if (lane < CT) {
         const float G = sG[lane], GC = sG[CT - 1];
-        sCk[lane] = sRk[lane] * __expf(G);
-        sCq[lane] = a.scale * sRq[lane] * __expf(G);
-        sCu[lane] = sRk[lane] * __expf(GC - G);
+        sCk[lane] = sRk[lane] * exp2f_hw(G);
+        sCq[lane] = a.scale * sRq[lane] * exp2f_hw(G);
+        sCu[lane] = sRk[lane] * exp2f_hw(GC - G);
       }
     }
     if (wave == (C::NW > 1 ? 1 : 0)) {
@@ -513,7 +524,7 @@ chunked_prefill_kernel(const ScanArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const bool on = ib + r <= c;
-          const float f = rt * Ri[r] * __expf(on ? gt - Gi[r] : 0.f) * acc[4 * q4 + r];
+          const float f = rt * Ri[r] * exp2f_hw(on ? gt - Gi[r] : 0.f) * acc[4 * q4 + r];
           pv4[r] = on ? f : 0.f;
         }
         *reinterpret_cast<u32x2*>(sP + c * LDT + ib) =
@@ -547,9 +558,10 @@ chunked_prefill_kernel(const ScanArgs a) {
 #pragma unroll
         for (int u = 0; u < SB; ++u)
 #pragma unroll
-          for (int m4 = 0; m4 < MPL; m4 += 4) {
-            const float4 x = *reinterpret_cast<const float4*>(ab + (SB * bt + u) * LDA + m4);
-            dst[u][m4] = x.x; dst[u][m4 + 1] = x.y; dst[u][m4 + 2] = x.z; dst[u][m4 + 3] = x.w;
+          for (int p4 = 0; p4 < MPL; p4 += 4) {   // part rows MPL-1-p4 .. MPL-4-p4
+            const float4 x = *reinterpret_cast<const float4*>(ab + (SB * bt + u) * LDA + p4);
+            dst[u][MPL - 1 - p4] = x.x; dst[u][MPL - 2 - p4] = x.y;
+            dst[u][MPL - 3 - p4] = x.z; dst[u][MPL - 4 - p4] = x.w;
           }
       };
       load_batch(col[0], 0);
@@ -635,7 +647,7 @@ chunked_prefill_kernel(const ScanArgs a) {
 #pragma unroll
         for (int ks = 0; ks < DK / 16; ++ks) kta[ks] = ldt(ks / 2, ks % 2);
       // S = e^{G_C} S + K^T (r_k e^{G_C - G} U); K^T rows from the transposed tile
-      const float gC = __expf(sG[CT - 1]);
+      const float gC = exp2f_hw(sG[CT - 1]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
