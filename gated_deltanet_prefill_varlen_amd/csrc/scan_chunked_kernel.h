@@ -74,6 +74,18 @@ __device__ __forceinline__ uint32_t pack_f16(float x0, float x1) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, f16x2));
 }
 
+// Four fp16 values by an LDS transpose read (ds_read_b64_tr_b16).  Within
+// each group of 16 lanes, lane l names an 8-byte piece P_l (4 elements);
+// lane i receives element i % 4 of P_{i/4}, P_{i/4+4}, P_{i/4+8}, P_{i/4+12}
+// (lane layout checked on the GPU with an in-bounds probe).  With lane
+// 4j + r naming columns 4r .. 4r+3 of row j of a row-major tile, lane i gets
+// column i of rows 0..3: a 16-column x 4-row block, transposed.
+__device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 LdsS16x4;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS16x4*)p));
+}
+
 // Accumulator half h2 (registers 8h2..8h2+7) as a B operand.
 template <int H2>
 __device__ __forceinline__ f16x8 acc_half(const f32x16& x) {
@@ -150,7 +162,6 @@ struct Cfg {
   static constexpr int NTH = 64 * NW;     // threads
   static constexpr int KT = DK / 32;      // 32-wide k tiles of the state
   static constexpr int LDK = DK + 4;      // row stride of sK, sQ (fp16; 8-byte aligned rows)
-  static constexpr int LDKT = CT + 4;     // row stride of sKt, the transposed K tile (fp16)
   static constexpr int LDT = CT + 4;      // row stride of sT, sP (fp16)
   static constexpr int LDV = DV + 8;      // row stride of the V / O tile (bf16; 16-byte rows)
   static constexpr int LDA = CT + 4;      // row stride of sA, A transposed (fp32)
@@ -166,8 +177,7 @@ struct Cfg {
   static constexpr int MPL = CT / LPC;    // rows of a column held per lane
   static constexpr int oK = 0;
   static constexpr int oQ = oK + CT * LDK * 2;
-  static constexpr int oKt = oQ + CT * LDK * 2;
-  static constexpr int oV = oKt + DK * LDKT * 2;      // V tile, then the O tile
+  static constexpr int oV = oQ + CT * LDK * 2;        // V tile, then the O tile
   static constexpr int oT = oV + CT * LDV * 2;
   static constexpr int oP = oT + CT * LDT * 2;
   static constexpr int oA = oP + CT * LDT * 2;
@@ -176,7 +186,7 @@ struct Cfg {
   static constexpr int bytes = oS + kScal * CT * 4;
   static_assert(bytes <= 80 * 1024, "two workgroups per CU");
   static_assert(NW <= 4 && LPC * CT <= SUBT, "wave roles");
-  static_assert(oQ % 16 == 0 && oKt % 16 == 0 && oV % 16 == 0 && oT % 16 == 0 && oA % 16 == 0, "align");
+  static_assert(oQ % 16 == 0 && oV % 16 == 0 && oT % 16 == 0 && oA % 16 == 0, "align");
   // the next chunk's rows wait in registers (16-byte vectors per thread)
   // while this chunk computes, when they fit in 32 registers
   // K and Q come in cells of 4 tokens x 4 key dims (four 8-byte row pieces),
@@ -194,12 +204,11 @@ template <int DK, int DV>
 __global__ void __launch_bounds__(64 * (DV / 32), 2)
 chunked_prefill_kernel(const ScanArgs a) {
   using C = Cfg<DK, DV>;
-  constexpr int CT = C::CT, NTH = C::NTH, KT = C::KT, LDK = C::LDK, LDKT = C::LDKT, LDT = C::LDT;
+  constexpr int CT = C::CT, NTH = C::NTH, KT = C::KT, LDK = C::LDK, LDT = C::LDT;
   constexpr int LDA = C::LDA, LPC = C::LPC, MPL = C::MPL, LDV = C::LDV;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* sK = reinterpret_cast<uint16_t*>(smem + C::oK);
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + C::oQ);
-  uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + C::oKt);
   uint16_t* sV = reinterpret_cast<uint16_t*>(smem + C::oV);
   uint16_t* sT = reinterpret_cast<uint16_t*>(smem + C::oT);
   uint16_t* sP = reinterpret_cast<uint16_t*>(smem + C::oP);
@@ -224,6 +233,12 @@ chunked_prefill_kernel(const ScanArgs a) {
   uint16_t* og = static_cast<uint16_t*>(a.out) + (size_t)h * DV;
   const size_t sstride = (size_t)a.Hv * DV * DK;
   const int v = 32 * wave + c;       // this lane's state column (value dim)
+  // K^T operands of the state update come from the row-major K tile by
+  // transpose reads: the lanes of 16-lane group grp cover key columns
+  // 16 (grp % 2) .. +15 of a 32-column tile and tokens 4 (grp / 2) + j; lane
+  // 4j + r names the 4-column piece r of token row j
+  const int grp = lane >> 4, li = lane & 15;
+  const uint16_t* ktr = sK + (4 * (grp >> 1) + (li >> 2)) * LDK + 16 * (grp & 1) + 4 * (li & 3);
 
   // ---- state slice S^T[k][v] for v in this wave's 32 columns
   f32x16 S[KT];
@@ -369,17 +384,14 @@ chunked_prefill_kernel(const ScanArgs a) {
   for (int t0 = seq0; t0 < seq1; t0 += a.chunk) {
     const int n = min(a.chunk, seq1 - t0);   // valid rows of this chunk
 
-    // ---- 1. stage K (row-major and transposed) and Q rows as fp16 (zero past
-    //         n) with their L2 norms (squares summed in registers, then over
+    // ---- 1. stage K and Q rows as fp16 (zero past n) with their L2 norms (squares summed in registers, then over
     //         the row's lanes), V rows, betas and the gate cumsum.  The rows
     //         were fetched into registers while the previous chunk ran.  The
     //         previous chunk's O rows leave the V/O tile first: read into
     //         registers before V lands, stored to HBM after.
     if constexpr (!C::PREFETCH) ld_gb(t0, n, pg, pb);
     {
-      // a cell: four 8-byte row pieces of K and of Q, converted to fp16; K
-      // goes to LDS row-major and, transposed in registers, as four 8-byte
-      // pieces of four tokens.
+      // a cell: four 8-byte row pieces of K and of Q, converted to fp16.
       // A token's squares are summed over its KC lanes (a fixed-order DPP sum
       // ending in the group's last lane).
       constexpr int KC = C::KC;
@@ -405,17 +417,6 @@ chunked_prefill_kernel(const ScanArgs a) {
             x.q[r] = bf16x4_to_f16(x.q[r], sq[r]);
             *reinterpret_cast<u32x2*>(sK + t * LDK + 4 * kc) = x.k[r];
             *reinterpret_cast<u32x2*>(sQ + t * LDK + 4 * kc) = x.q[r];
-          }
-          // transposed: key dim 4 kc + d, tokens 4 tg .. 4 tg + 3
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const int hw = d & 1;
-            auto part = [&](int r) { return d < 2 ? x.k[r].x : x.k[r].y; };
-            const uint32_t w0 = hw ? (part(0) >> 16) | (part(1) & 0xFFFF0000u)
-                                   : (part(0) & 0xFFFFu) | (part(1) << 16);
-            const uint32_t w1 = hw ? (part(2) >> 16) | (part(3) & 0xFFFF0000u)
-                                   : (part(2) & 0xFFFFu) | (part(3) << 16);
-            *reinterpret_cast<u32x2*>(sKt + (4 * kc + d) * LDKT + 4 * tg) = u32x2{w0, w1};
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -642,11 +643,15 @@ chunked_prefill_kernel(const ScanArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sV[acc_row(i, g) * LDV + v] = bf16_bits(QS[i]);
       f16x8 kta[NKS];
-      auto ldt = [&](int kt, int h2) { return lds_op(sKt + (32 * kt + c) * LDKT + 16 * h2 + 4 * g); };
+      auto ldt = [&](int kt, int h2) {   // K^T rows 32 kt + c, tokens as in lds_op
+        const uint16_t* p = ktr + 16 * h2 * LDK + 32 * kt;
+        const u32x2 lo = lds_tr4(p), hi = lds_tr4(p + 8 * LDK);
+        return __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      };
       if constexpr (PRE)
 #pragma unroll
         for (int ks = 0; ks < DK / 16; ++ks) kta[ks] = ldt(ks / 2, ks % 2);
-      // S = e^{G_C} S + K^T (r_k e^{G_C - G} U); K^T rows from the transposed tile
+      // S = e^{G_C} S + K^T (r_k e^{G_C - G} U); K^T rows by transpose reads
       const float gC = exp2f_hw(sG[CT - 1]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
