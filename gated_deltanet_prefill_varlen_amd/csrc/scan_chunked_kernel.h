@@ -148,9 +148,14 @@ __device__ __forceinline__ float group_bcast(float x) {
   }
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Two fp32 values as packed bf16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, b2));
+}
 
 // Row of accumulator register i for lane half g.
 __device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
@@ -177,12 +182,12 @@ struct Cfg {
   static constexpr int MPL = CT / LPC;    // rows of a column held per lane
   static constexpr int oK = 0;
   static constexpr int oQ = oK + CT * LDK * 2;
-  static constexpr int oV = oQ + CT * LDK * 2;        // V tile, then the O tile
+  static constexpr int oV = oQ + CT * LDK * 2;        // V tile
   static constexpr int oT = oV + CT * LDV * 2;
   static constexpr int oP = oT + CT * LDT * 2;
   static constexpr int oA = oP + CT * LDT * 2;
   static constexpr int oS = oA + CT * LDA * 4;        // per-token scalars
-  static constexpr int kScal = 8;
+  static constexpr int kScal = 12;
   static constexpr int bytes = oS + kScal * CT * 4;
   static_assert(bytes <= 80 * 1024, "two workgroups per CU");
   static_assert(NW <= 4 && LPC * CT <= SUBT, "wave roles");
@@ -198,7 +203,7 @@ struct Cfg {
 };
 
 // per-token scalar arrays (index into the scalar block)
-enum { SC_G = 0, SC_BETA, SC_RK, SC_RQ, SC_CK, SC_CQ, SC_CU, SC_PAD };
+enum { SC_G = 0, SC_BETA, SC_RK, SC_RQ, SC_CK, SC_CQ, SC_CU, SC_LA, SC_LK0, SC_LQ, SC_LK1, SC_PAD };
 
 template <int DK, int DV>
 __global__ void __launch_bounds__(64 * (DV / 32), 2)
@@ -221,6 +226,14 @@ chunked_prefill_kernel(const ScanArgs a) {
   float* sCk = sc + SC_CK * CT;     // r_k e^G
   float* sCq = sc + SC_CQ * CT;     // scale r_q e^G
   float* sCu = sc + SC_CU * CT;     // r_k e^{G_C - G}
+  // base-2 exponents of the Gram and K Q^T factors: beta_t r_t r_i e^{G_t-G_i}
+  // = 2^(LA_t - LK_i) and r_q,t r_k,i e^{G_t-G_i} = 2^(LQ_t - LK_i), with
+  // LA = G + log2(beta r_k), LQ = G + log2(r_q), LK = G - log2(r_k) (G in
+  // base 2); one copy of LK per role wave
+  float* sLA = sc + SC_LA * CT;
+  float* sLK0 = sc + SC_LK0 * CT;
+  float* sLQ = sc + SC_LQ * CT;
+  float* sLK1 = sc + SC_LK1 * CT;
 
   const int s = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -330,8 +343,11 @@ chunked_prefill_kernel(const ScanArgs a) {
   constexpr bool PRE = C::NW > 1;
   constexpr int NKS = PRE ? DK / 16 : 1;
 
-  // X = K S0^T and QS = Q S0^T for this wave's columns, S0 rounded to fp16
-  // per k tile on the fly
+  // X = K S0^T (rows t, lane column v) and QS = S0 Q^T (rows v, lane column
+  // t: the output tile comes out transposed, one token per lane) for this
+  // wave's columns, S0 rounded to fp16 per k tile on the fly; an
+  // accumulator half serves as the A operand (row v) as well as the B
+  // operand (column v)
   auto xqs = [&](f32x16& X, f32x16& QS) {
     f16x8 ka[NKS], qa[NKS];
     auto ld = [&](int ks, f16x8& kx, f16x8& qx) {
@@ -354,7 +370,7 @@ chunked_prefill_kernel(const ScanArgs a) {
         const f16x8& qx = qa[PRE ? ks : 0];
         const f16x8 sh = h2 == 0 ? acc_half<0>(S[kt]) : acc_half<1>(S[kt]);
         X = mma(kx, sh, X);
-        QS = mma(qx, sh, QS);
+        QS = mma(sh, qx, QS);
       }
   };
 
@@ -380,15 +396,15 @@ chunked_prefill_kernel(const ScanArgs a) {
     return acc;
   };
 
-  int pt0 = 0, pn = 0;   // previous chunk: its O tile is still in the V/O LDS tile
+  // byte offset of this lane's output piece in a chunk's first row: token c,
+  // columns 32 w + 4 g ..
+  const uint32_t o_lane = __umul24((uint32_t)c, hv * (2 * DV)) + 2 * (32 * wave + 4 * g);
   for (int t0 = seq0; t0 < seq1; t0 += a.chunk) {
     const int n = min(a.chunk, seq1 - t0);   // valid rows of this chunk
 
     // ---- 1. stage K and Q rows as fp16 (zero past n) with their L2 norms (squares summed in registers, then over
     //         the row's lanes), V rows, betas and the gate cumsum.  The rows
-    //         were fetched into registers while the previous chunk ran.  The
-    //         previous chunk's O rows leave the V/O tile first: read into
-    //         registers before V lands, stored to HBM after.
+    //         were fetched into registers while the previous chunk ran.
     if constexpr (!C::PREFETCH) ld_gb(t0, n, pg, pb);
     {
       // a cell: four 8-byte row pieces of K and of Q, converted to fp16.
@@ -436,19 +452,15 @@ chunked_prefill_kernel(const ScanArgs a) {
       }
     }
     {
-      // a thread owns the same 16-byte segments of the V/O tile for both
-      u32x4 ov[C::NVV];
 #pragma unroll
       for (int u = 0; u < C::NVV; ++u) {
         const int e = tid + u * NTH;
         if (e < CT * DV / 8) {
           const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-          u32x4* seg = reinterpret_cast<u32x4*>(sV + t * LDV + c8);
           u32x4 vx;
           if constexpr (C::PREFETCH) vx = pv[u]; else ld_v(u, t0, n, vx);
-          ov[u] = *seg;
           if (n < CT && t >= n) vx = u32x4{0u, 0u, 0u, 0u};
-          *seg = vx;
+          *reinterpret_cast<u32x4*>(sV + t * LDV + c8) = vx;
         }
       }
       if (wave == 0) {  // betas and the inclusive scan of the log-gates (fixed order),
@@ -458,14 +470,6 @@ chunked_prefill_kernel(const ScanArgs a) {
           sG[lane] = x;
           sBeta[lane] = lane < n ? pb : 0.f;
         }
-      }
-#pragma unroll
-      for (int u = 0; u < C::NVV; ++u) {
-        const int e = tid + u * NTH;
-        const uint32_t t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-        if (e < CT * DV / 8 && (int)t < pn)
-          *reinterpret_cast<u32x4*>(const_cast<char*>(row(og + (size_t)pt0 * a.Hv * DV,
-                                                          __umul24(t, hv * (2 * DV)) + 2 * c8))) = ov[u];
       }
     }
     __syncthreads();
@@ -483,22 +487,26 @@ chunked_prefill_kernel(const ScanArgs a) {
       // parts of the substitution, each part's rows in descending order:
       // (t, i) at i*LDA + (t % LPC)*MPL + MPL - 1 - t / LPC.  The rows a
       // substitution step still needs are then an aligned prefix of the part.
+      // (the exponents are formed while the MFMA chain runs; beta = 0 gives
+      // LA = -inf and a zero factor; masked entries may overflow and are
+      // replaced by the select)
+      if (lane < CT) {
+        const float G = sG[lane], lr = __builtin_amdgcn_logf(sRk[lane]);
+        sLA[lane] = G + (__builtin_amdgcn_logf(sBeta[lane]) + lr);
+        sLK0[lane] = G - lr;
+      }
       const f32x16 acc = rows_mm(sK, sK);
-      const float gi = sG[c], ri = sRk[c];
+      const float lki = sLK0[c];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int tb = 8 * q4 + 4 * g;
-        const float4 G4 = *reinterpret_cast<const float4*>(sG + tb);
-        const float4 B4 = *reinterpret_cast<const float4*>(sBeta + tb);
-        const float4 R4 = *reinterpret_cast<const float4*>(sRk + tb);
-        const float Gr[4] = {G4.x, G4.y, G4.z, G4.w}, Br[4] = {B4.x, B4.y, B4.z, B4.w};
-        const float Rr[4] = {R4.x, R4.y, R4.z, R4.w};
+        const float4 L4 = *reinterpret_cast<const float4*>(sLA + tb);
+        const float La[4] = {L4.x, L4.y, L4.z, L4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = tb + r;
-          const bool on = c < t;
-          const float f = Br[r] * Rr[r] * ri * exp2f_hw(on ? Gr[r] - gi : 0.f) * acc[4 * q4 + r];
-          sA[c * LDA + (t % LPC) * MPL + MPL - 1 - t / LPC] = on ? f : 0.f;
+          const float f = exp2f_hw(La[r] - lki) * acc[4 * q4 + r];
+          sA[c * LDA + (t % LPC) * MPL + MPL - 1 - t / LPC] = c < t ? f : 0.f;
         }
       }
       if (lane < CT) {
@@ -513,20 +521,23 @@ chunked_prefill_kernel(const ScanArgs a) {
       // rows (lane column = query t = c); P[t][i] = scale r_q,t r_k,i
       // e^{G_t - G_i} q_t.k_i for i <= t, written as row t of P (fp16), four
       // keys per 8-byte store
+      if (lane < CT) {
+        const float G = sG[lane];
+        sLQ[lane] = G + __builtin_amdgcn_logf(sRq[lane]);
+        sLK1[lane] = G - __builtin_amdgcn_logf(sRk[lane]);
+      }
       const f32x16 acc = rows_mm(sK, sQ);
-      const float gt = sG[c], rt = a.scale * sRq[c];
+      const float lqt = sLQ[c];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int ib = 8 * q4 + 4 * g;
-        const float4 G4 = *reinterpret_cast<const float4*>(sG + ib);
-        const float4 R4 = *reinterpret_cast<const float4*>(sRk + ib);
-        const float Gi[4] = {G4.x, G4.y, G4.z, G4.w}, Ri[4] = {R4.x, R4.y, R4.z, R4.w};
+        const float4 L4 = *reinterpret_cast<const float4*>(sLK1 + ib);
+        const float Lk[4] = {L4.x, L4.y, L4.z, L4.w};
         float pv4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool on = ib + r <= c;
-          const float f = rt * Ri[r] * exp2f_hw(on ? gt - Gi[r] : 0.f) * acc[4 * q4 + r];
-          pv4[r] = on ? f : 0.f;
+          const float f = a.scale * exp2f_hw(lqt - Lk[r]) * acc[4 * q4 + r];
+          pv4[r] = ib + r <= c ? f : 0.f;
         }
         *reinterpret_cast<u32x2*>(sP + c * LDT + ib) =
             u32x2{pack_f16(pv4[0], pv4[1]), pack_f16(pv4[2], pv4[3])};
@@ -630,18 +641,24 @@ chunked_prefill_kernel(const ScanArgs a) {
       };
       // U = T Y
       f32x16 U = tri_mm(tA, X, f32x16{});
-      // O = scale r_q e^G (Q S0^T) + P U, into this wave's own columns of the
-      // V/O tile (V of these columns was consumed above by this wave only);
-      // stored out next chunk
+      // O^T = scale r_q e^G (S0 Q^T) + U^T P^T: rows v, lane column token
+      // t = c; the P row operands of token t serve as the B operand
+      {
+        const float cq = sCq[c];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 c4 = *reinterpret_cast<const float4*>(sCq + 8 * q4 + 4 * g);
-        QS[4 * q4] *= c4.x; QS[4 * q4 + 1] *= c4.y;
-        QS[4 * q4 + 2] *= c4.z; QS[4 * q4 + 3] *= c4.w;
+        for (int i = 0; i < 16; ++i) QS[i] *= cq;
       }
-      QS = tri_mm(pA, U, QS);
+      QS = mma(acc_half<0>(U), pA[0], QS);
+      QS = mma(acc_half<1>(U), pA[1], QS);
+      // token t's columns 32w + 8 q4 + 4 g .. +3 as 8-byte bf16 pieces,
+      // straight to HBM
+      if (c < n) {
+        char* orow = const_cast<char*>(row(og + (size_t)t0 * a.Hv * DV, o_lane));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sV[acc_row(i, g) * LDV + v] = bf16_bits(QS[i]);
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<u32x2*>(orow + 16 * q4) =
+              u32x2{pack_bf16(QS[4 * q4], QS[4 * q4 + 1]), pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3])};
+      }
       f16x8 kta[NKS];
       auto ldt = [&](int kt, int h2) {   // K^T rows 32 kt + c, tokens as in lds_op
         const uint16_t* p = ktr + 16 * h2 * LDK + 32 * kt;
@@ -678,15 +695,7 @@ chunked_prefill_kernel(const ScanArgs a) {
       ci = __builtin_amdgcn_readfirstlane(ci + 1);
       next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
     }
-    pt0 = t0;
-    pn = n;
     __syncthreads();
-  }
-  for (int e = tid; e < CT * DV / 8; e += NTH) {   // last chunk's O rows
-    const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-    if (t < pn)
-      *reinterpret_cast<u32x4*>(og + (size_t)(pt0 + t) * a.Hv * DV + c8) =
-          *reinterpret_cast<const u32x4*>(sV + t * LDV + c8);
   }
   if (a.final_state) store_state(a.final_state + (size_t)s * sstride + ((size_t)h * DV + v) * DK);
 }
