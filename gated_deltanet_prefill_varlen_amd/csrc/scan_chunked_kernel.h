@@ -182,7 +182,7 @@ struct Cfg {
   static constexpr int MPL = CT / LPC;    // rows of a column held per lane
   static constexpr int oK = 0;
   static constexpr int oQ = oK + CT * LDK * 2;
-  static constexpr int oV = oQ + CT * LDK * 2;        // V tile
+  static constexpr int oV = oQ + CT * LDK * 2;        // V tile, then the O tile
   static constexpr int oT = oV + CT * LDV * 2;
   static constexpr int oP = oT + CT * LDT * 2;
   static constexpr int oA = oP + CT * LDT * 2;
@@ -396,15 +396,15 @@ chunked_prefill_kernel(const ScanArgs a) {
     return acc;
   };
 
-  // byte offset of this lane's output piece in a chunk's first row: token c,
-  // columns 32 w + 4 g ..
-  const uint32_t o_lane = __umul24((uint32_t)c, hv * (2 * DV)) + 2 * (32 * wave + 4 * g);
+  int pt0 = 0, pn = 0;   // previous chunk: its O rows are still in the V/O tile
   for (int t0 = seq0; t0 < seq1; t0 += a.chunk) {
     const int n = min(a.chunk, seq1 - t0);   // valid rows of this chunk
 
     // ---- 1. stage K and Q rows as fp16 (zero past n) with their L2 norms (squares summed in registers, then over
     //         the row's lanes), V rows, betas and the gate cumsum.  The rows
-    //         were fetched into registers while the previous chunk ran.
+    //         were fetched into registers while the previous chunk ran.  The
+    //         previous chunk's O rows leave the V/O tile first: read into
+    //         registers before V lands, stored to HBM after.
     if constexpr (!C::PREFETCH) ld_gb(t0, n, pg, pb);
     {
       // a cell: four 8-byte row pieces of K and of Q, converted to fp16.
@@ -452,15 +452,19 @@ chunked_prefill_kernel(const ScanArgs a) {
       }
     }
     {
+      // a thread owns the same 16-byte segments of the V/O tile for both
+      u32x4 ov[C::NVV];
 #pragma unroll
       for (int u = 0; u < C::NVV; ++u) {
         const int e = tid + u * NTH;
         if (e < CT * DV / 8) {
           const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+          u32x4* seg = reinterpret_cast<u32x4*>(sV + t * LDV + c8);
           u32x4 vx;
           if constexpr (C::PREFETCH) vx = pv[u]; else ld_v(u, t0, n, vx);
+          ov[u] = *seg;
           if (n < CT && t >= n) vx = u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(sV + t * LDV + c8) = vx;
+          *seg = vx;
         }
       }
       if (wave == 0) {  // betas and the inclusive scan of the log-gates (fixed order),
@@ -470,6 +474,14 @@ chunked_prefill_kernel(const ScanArgs a) {
           sG[lane] = x;
           sBeta[lane] = lane < n ? pb : 0.f;
         }
+      }
+#pragma unroll
+      for (int u = 0; u < C::NVV; ++u) {
+        const int e = tid + u * NTH;
+        const uint32_t t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+        if (e < CT * DV / 8 && (int)t < pn)
+          *reinterpret_cast<u32x4*>(const_cast<char*>(row(og + (size_t)pt0 * a.Hv * DV,
+                                                          __umul24(t, hv * (2 * DV)) + 2 * c8))) = ov[u];
       }
     }
     __syncthreads();
@@ -610,12 +622,23 @@ chunked_prefill_kernel(const ScanArgs a) {
       // the LDS operands of the stage are requested ahead of their use, so the
       // LDS round trips overlap: V of this wave's columns first, then the T
       // and P row operands, the K^T row operands of the update (with several
-      // waves) once O is out
+      // waves) once O is out.  V comes by four transpose reads of the
+      // row-major V tile (as the K^T operands do): lane (c, g) gets column v
+      // of rows 8 q4 + 4 g .. +3, the accumulator rows of registers 4q4..4q4+3.
       const uint16_t* tr = sT + c * LDT + 4 * g;
       const uint16_t* pr = sP + c * LDT + 4 * g;
       float vv[16];
+      {
+        const uint16_t* vtr = sV + (4 * (grp >> 1) + (li >> 2)) * LDV + 32 * wave + 16 * (grp & 1) + 4 * (li & 3);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vv[i] = bf16_to_f32(sV[acc_row(i, g) * LDV + v]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const u32x2 w = lds_tr4(vtr + 8 * q4 * LDV);
+          vv[4 * q4] = __uint_as_float(w.x << 16);
+          vv[4 * q4 + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+          vv[4 * q4 + 2] = __uint_as_float(w.y << 16);
+          vv[4 * q4 + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
       const f16x8 tA[2] = {lds_op(tr), lds_op(tr + 16)};
 
@@ -650,15 +673,13 @@ chunked_prefill_kernel(const ScanArgs a) {
       }
       QS = mma(acc_half<0>(U), pA[0], QS);
       QS = mma(acc_half<1>(U), pA[1], QS);
-      // token t's columns 32w + 8 q4 + 4 g .. +3 as 8-byte bf16 pieces,
-      // straight to HBM
-      if (c < n) {
-        char* orow = const_cast<char*>(row(og + (size_t)t0 * a.Hv * DV, o_lane));
+      // token t's columns 32w + 8 q4 + 4 g .. +3 as 8-byte bf16 pieces into
+      // this wave's own columns of the V/O tile (their V was consumed above
+      // by this wave only); the rows go to HBM in the next chunk's staging
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<u32x2*>(orow + 16 * q4) =
-              u32x2{pack_bf16(QS[4 * q4], QS[4 * q4 + 1]), pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3])};
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<u32x2*>(sV + c * LDV + 32 * wave + 8 * q4 + 4 * g) =
+            u32x2{pack_bf16(QS[4 * q4], QS[4 * q4 + 1]), pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3])};
       f16x8 kta[NKS];
       auto ldt = [&](int kt, int h2) {   // K^T rows 32 kt + c, tokens as in lds_op
         const uint16_t* p = ktr + 16 * h2 * LDK + 32 * kt;
@@ -695,7 +716,15 @@ chunked_prefill_kernel(const ScanArgs a) {
       ci = __builtin_amdgcn_readfirstlane(ci + 1);
       next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
     }
+    pt0 = t0;
+    pn = n;
     __syncthreads();
+  }
+  for (int e = tid; e < CT * DV / 8; e += NTH) {   // last chunk's O rows
+    const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+    if (t < pn)
+      *reinterpret_cast<u32x4*>(og + (size_t)(pt0 + t) * a.Hv * DV + c8) =
+          *reinterpret_cast<const u32x4*>(sV + t * LDV + c8);
   }
   if (a.final_state) store_state(a.final_state + (size_t)s * sstride + ((size_t)h * DV + v) * DK);
 }
