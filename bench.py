@@ -181,6 +181,96 @@ def bench_prefill(torch, gdn, p, steps, warmup, stream, flush, label):
     return res, times
 
 
+def conv_alg_bytes(T: int, N: int, C: int, n_ckpt: int, e: int = 2) -> int:
+    """Bytes the conv must move: x in, y out, weights, each prompt's conv state
+    (last three inputs) and the three-input window at each checkpoint."""
+    return 2 * T * C * e + C * 4 * 4 + (N + n_ckpt) * 3 * C * e
+
+
+def bench_layer_step(torch, gdn, p, steps, warmup, stream, flush, label):
+    """One pass of the whole hot path over the chat wave: the packed conv1d +
+    SiLU from the pre-conv rows x into one [T, conv_dim] tensor (with the
+    prompts' conv states and the conv windows at the checkpoints), the scan
+    reading q, k, v as column views of it (checkpoints into a device buffer),
+    then the checkpoint copy into a device pool on its own stream after an
+    event, joined back before the step's closing event.  Events around the
+    scan launch give the scan kernel's own time for its roofline."""
+    T, N = p.n_tokens, p.n_seqs
+    C = 2 * p.Hqk * p.dk + p.Hv * p.dv
+    ck = gdn.gdn_plan_checkpoints(p.cu_seqlens, p.block)
+    n_ck = len(ck)
+    x = io_t(torch, p.x, p.dtype)
+    w = f32_t(torch, p.conv_w)
+    y = torch.empty_like(x)
+    conv_state = torch.empty((N, 3, C), dtype=x.dtype, device="cuda:0")
+    conv_ckpt = torch.empty((n_ck, 3, C), dtype=x.dtype, device="cuda:0")
+    cu_d, ck_d = i32_t(torch, p.cu_seqlens), i32_t(torch, ck)
+    g, beta = f32_t(torch, p.g), f32_t(torch, p.beta)
+    qv, kv, vv = y[:, :p.Hqk * p.dk], y[:, p.Hqk * p.dk:2 * p.Hqk * p.dk], y[:, 2 * p.Hqk * p.dk:]
+    out = torch.empty((T, p.Hv, p.dv), dtype=x.dtype, device="cuda:0")
+    final = torch.empty((N, p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
+    ckbuf = torch.empty((n_ck, p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
+    pool_slots = n_ck + 32
+    pool = torch.empty((pool_slots, p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
+    slots = np.random.default_rng(0).permutation(pool_slots)[:n_ck].astype(np.int64)
+    slots_d = torch.from_numpy(slots).to("cuda:0")
+    each = p.Hv * p.dv * p.dk * 4
+    shape = gdn.make_shape(p.Hqk, p.Hv, p.dk, p.dv, p.chunk,
+                           gdn.GDN_BF16 if p.dtype == "bf16" else gdn.GDN_F32, scale=p.scale,
+                           q_tok_stride=C, k_tok_stride=C, v_tok_stride=C)
+    cstream = torch.cuda.Stream()
+    scan_done, copy_done = torch.cuda.Event(), torch.cuda.Event()
+
+    def step(ev=None):
+        gdn.gdn_conv1d_silu_packed(shape, cu_d, p.cu_seqlens, x, w, y, None, conv_state, ck_d, ck,
+                                   conv_ckpt, stream=stream)
+        if ev:
+            ev[0].record(stream)
+        gdn.gdn_prefill_packed(shape, cu_d, p.cu_seqlens, qv, kv, vv, g, beta, None, ck_d, ck,
+                               out, final, ckbuf, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        scan_done.record(stream)
+        gdn.gdn_snapshot_copy(ckbuf, n_ck, each, pool, slots_d, slots, pool_slots, wait_event=scan_done,
+                              copy_stream=cstream, done_event=copy_done)
+        stream.wait_event(copy_done)
+
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(steps):
+            flush()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            step(e[1:3])
+            e[3].record(stream)
+            evs.append(e)
+        evs[-1][3].synchronize()
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(d) for a, b, c, d in evs]
+    scan_ms = [b.elapsed_time(c) for a, b, c, d in evs]
+    conv_ms = [a.elapsed_time(b) for a, b, c, d in evs]
+    med = statistics.median(step_ms)
+    B_scan = prefill_alg_bytes(p, n_ck, p.init is not None)
+    B_conv = conv_alg_bytes(T, N, C, n_ck)
+    B_copy = 2 * n_ck * each
+    F = prefill_alg_flops(p)
+    exact = bool(torch.equal(pool[slots_d], ckbuf))
+    return {
+        "workload": label, "tokens": T, "prompts": N, "checkpoints": int(n_ck),
+        "ms_median": med, "ms_mean": statistics.fmean(step_ms),
+        "ms_p10": float(np.percentile(step_ms, 10)), "ms_p90": float(np.percentile(step_ms, 90)),
+        "tokens_per_s": T / (med * 1e-3),
+        "conv_ms_median": statistics.median(conv_ms),
+        "scan_ms_median": statistics.median(scan_ms), "scan_ms_mean": statistics.fmean(scan_ms),
+        "scan_alg_bytes": B_scan, "scan_alg_flops": F,
+        "step_alg_bytes": B_scan + B_conv + B_copy,
+        "copy_exact": exact,
+    }
+
+
 def bench_conv(torch, gdn, stream, flush, reps):
     T, Hqk, Hv, d = 32768, 16, 32, 128
     C = 2 * Hqk * d + Hv * d
@@ -406,8 +496,14 @@ def _oracle_one_prompt(args):
     from threadpoolctl import threadpool_limits
     with threadpool_limits(1):
         import oracle as O
-        q, k, v, g, b = args
+        q, k, v, g, b, x, w = args
         t = time.perf_counter()
+        if x is not None:   # the whole path: conv1d+SiLU first, q, k, v are its column blocks
+            y = O.conv1d_silu_packed(x, w, [0, x.shape[0]])[0]
+            L, nq, nv = x.shape[0], q.shape[1] * q.shape[2], v.shape[1] * v.shape[2]
+            q = y[:, :nq].reshape(q.shape)
+            k = y[:, nq:2 * nq].reshape(k.shape)
+            v = y[:, 2 * nq:2 * nq + nv].reshape(v.shape)
         O.prefill_recurrent(q, k, v, g, b, [0, q.shape[0]])
         return time.perf_counter() - t
 
@@ -421,8 +517,10 @@ def cpu_baseline(p, n_prompts: int):
     jobs = []
     for s in range(n_prompts):
         sl = slice(int(p.cu_seqlens[s]), int(p.cu_seqlens[s + 1]))
+        x = None if p.x is None else O.to_f64(p.x[sl], p.dtype)
+        w = None if p.conv_w is None else p.conv_w.astype(np.float64)
         jobs.append((O.to_f64(p.q[sl], p.dtype), O.to_f64(p.k[sl], p.dtype), O.to_f64(p.v[sl], p.dtype),
-                     p.g[sl].astype(np.float64), p.beta[sl].astype(np.float64)))
+                     p.g[sl].astype(np.float64), p.beta[sl].astype(np.float64), x, w))
     ctx = mp.get_context("spawn")
     t0 = time.perf_counter()
     with ctx.Pool(procs) as pool:
@@ -438,8 +536,9 @@ def cpu_baseline(p, n_prompts: int):
     except OSError:
         pass
     return {"value": toks / wall, "unit": "tokens/s/layer", "cores": procs, "kind": "oracle",
-            "sample": f"{n_prompts} of the 32 prompts ({toks} tokens, all 32 heads), fp64 token-by-token "
-                      f"recurrence, one process per prompt; wall {wall:.1f} s; {cpu_model}",
+            "sample": f"{n_prompts} of the 32 prompts ({toks} tokens, all 32 heads), fp64 "
+                      + ("conv1d+SiLU then " if p.x is not None else "")
+                      + f"token-by-token recurrence, one process per prompt; wall {wall:.1f} s; {cpu_model}",
             "cpu_seconds": float(sum(per))}
 
 
@@ -480,15 +579,26 @@ def main():
         return
     fn, label = makers[args.workload]
     log(f"[bench] generating {label}")
-    p = fn(seed=0)
-    log("[bench] timing headline step")
+    p = fn(seed=0, with_conv=True) if args.workload == "chat" else fn(seed=0)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    head, times = bench_prefill(torch, gdn, p, args.steps, args.warmup, stream, flush, label)
+    if args.workload == "chat":
+        log("[bench] timing headline step (conv, scan, checkpoint copy)")
+        label += ": conv1d+SiLU, scan with checkpoints, checkpoint copy on its own stream"
+        step = bench_layer_step(torch, gdn, p, args.steps, args.warmup, stream, flush, label)
+        head = {"workload": label, "ms_median": step["ms_median"], "tokens_per_s": step["tokens_per_s"],
+                "ms_p10": step["ms_p10"], "ms_p90": step["ms_p90"], "checkpoints": step["checkpoints"],
+                "alg_bytes": step["scan_alg_bytes"], "alg_flops": step["scan_alg_flops"],
+                "scan_ms_mean": step["scan_ms_mean"], "step": step}
+    else:
+        log("[bench] timing headline step (scan)")
+        head, _ = bench_prefill(torch, gdn, p, args.steps, args.warmup, stream, flush, label)
+        head["scan_ms_mean"] = head["ms_mean"]
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
-    log(f"[bench] headline: {head['ms_median']:.3f} ms, {head['tokens_per_s']/1e6:.2f} M tok/s, "
-        f"{head['roofline_frac']*100:.1f}% of roofline")
+    scan_ach = head["alg_bytes"] / (head["scan_ms_mean"] * 1e-3) / 1e9
+    log(f"[bench] headline: {head['ms_median']:.3f} ms per step, {head['tokens_per_s']/1e6:.2f} M tok/s; "
+        f"scan {head['scan_ms_mean']:.3f} ms, {scan_ach / HBM_PEAK_GBS * 100:.1f}% of the HBM roofline")
 
     legs = {}
     if not args.no_legs:
@@ -498,6 +608,10 @@ def main():
                         ("mixed", bench_mixed), ("overlap", bench_overlap)):
             log(f"[bench] leg {name}")
             legs[name] = f(torch, gdn, stream, flush, 10)
+        if args.workload == "chat":
+            log("[bench] leg scan_only")
+            legs["scan_only"], _ = bench_prefill(torch, gdn, p, args.steps, args.warmup, stream, flush,
+                                                 makers["chat"][1] + ", scan alone (dense q, k, v)")
         for wname in ("long", "ragged"):
             if wname == args.workload:
                 continue
@@ -511,8 +625,7 @@ def main():
         log("[bench] CPU oracle baseline")
         cpu = cpu_baseline(p, args.cpu_prompts)
 
-    med_s = head["ms_median"] * 1e-3
-    mean_s = head["ms_mean"] * 1e-3
+    mean_s = head["scan_ms_mean"] * 1e-3
     achieved = head["alg_bytes"] / mean_s / 1e9
     line = {
         "metric": "packed GDN prefill tokens/s/layer (32x1K pack) + % of MFMA/HBM roofline",
@@ -530,14 +643,16 @@ def main():
         "config": {"workload": head["workload"], "tokens": p.n_tokens, "prompts": p.n_seqs,
                    "qk_heads": p.Hqk, "v_heads": p.Hv, "head_dim": p.dk, "chunk": p.chunk,
                    "checkpoint_block": p.block, "checkpoints": head["checkpoints"],
-                   "timing": "median of per-step HIP-event times on the launch stream; 1 GiB cache "
-                             "flush before each step, outside the events",
+                   "timing": "median of per-step HIP-event times on the launch stream (the copy "
+                             "stream joined before the closing event); 1 GiB cache flush before "
+                             "each step, outside the events",
                    "wall_s_timed_region": t_wall},
+        "step": head.get("step"),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(args.workload),
                      "kernel": "chunked_prefill_kernel<128,128>", "alg_bytes_per_launch": head["alg_bytes"],
-                     "launch_ms_mean": head["ms_mean"],
+                     "launch_ms_mean": head["scan_ms_mean"],
                      "mfma_alg_tflops": head["alg_flops"] / mean_s / 1e12},
         "cpu_baseline": cpu,
         "legs": legs,

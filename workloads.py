@@ -190,11 +190,12 @@ def tiny_pack(seed=0) -> Pack:
                      with_conv=True, conv_std=0.5)
 
 
-def chat_wave(seed=0, n_prompts=32, prompt_len=1024) -> Pack:
+def chat_wave(seed=0, n_prompts=32, prompt_len=1024, with_conv=False) -> Pack:
     """32 x 1,024-token chat prompts, 16 qk / 32 v heads, d = 128, bf16,
-    zero initial state, chunk 64, checkpoint every 256 tokens."""
+    zero initial state, chunk 64, checkpoint every 256 tokens; with_conv adds
+    the pre-conv rows x (q | k | v as drawn) and std-0.5 conv weights."""
     return make_pack("chat_wave_32x1024", [prompt_len] * n_prompts, 16, 32, 128, 128, 64, 256,
-                     seed=seed)
+                     seed=seed, with_conv=with_conv, conv_std=0.5)
 
 
 def _ragged_lengths(n=8, lo=17, hi=2048, cap=8192):
