@@ -189,3 +189,22 @@ def test_degenerate_inputs(case):
         np.testing.assert_array_equal(to_f64(dp.final), p.init.astype(np.float64))
     eo, es = assert_parity(dp, all_pairs(p))
     print(f"{case}: out {eo:.2e} state {es:.2e}")
+
+
+@pytest.mark.parametrize("qk_mul,v_mul", [(256.0, 64.0), (1.0 / 64, 1.0 / 64)])
+def test_input_scales(qk_mul, v_mul):
+    """Raw q/k and v scaled by powers of two (exact in bf16): the L2 norms
+    undo the q/k scale and the state follows v's, so the relative errors stay
+    those of unit-scale inputs while the fp16 operands sit far from 1.  (With
+    v at 1/1024 of unit scale the state's entries reach fp16's subnormal
+    range and the state error rises to 1.2e-3: the fp16 operand domain.)"""
+    p = W.make_pack("scales", [130, 64, 33], 2, 4, 128, 128, 64, 64, seed=41, init_std=0.1,
+                    unit_qk=False)
+    p.init = (p.init * v_mul).astype(np.float32)
+    for name, mul in (("q", qk_mul), ("k", qk_mul), ("v", v_mul)):
+        x = O.to_f64(getattr(p, name), "bf16") * mul
+        setattr(p, name, W.f32_to_bf16_bits(x.astype(np.float32)))
+    dp = DevPack(p, _ckpt(p)).run()
+    torch.cuda.synchronize()
+    eo, es = assert_parity(dp, all_pairs(p))
+    print(f"scales q,k x{qk_mul} v x{v_mul}: out {eo:.2e} state {es:.2e}")
