@@ -165,6 +165,13 @@ GDN_API gdn_status gdn_conv1d_silu_packed(const gdn_shape* shape, const int32_t*
  *   out:              device io_dtype [n_tokens, Hv, dv] (dense).
  *   final_state:      device fp32 [n_seqs, Hv, dv, dk] or NULL (not written).
  *   ckpt_buf:         device fp32 [n_ckpt, Hv, dv, dk]; may be NULL iff n_ckpt = 0.
+ * Arithmetic: states are carried and accumulated in fp32.  With bf16 io the
+ * scan's products run on fp16 matrix-core operands: the raw q/k rows convert
+ * to fp16 exactly, the fp32 values entering a product (state, T, P, Y, U) are
+ * rounded to fp16 once, which holds states to about 4e-4 relative Frobenius
+ * against exact arithmetic while q/k elements, the state's entries and the
+ * update values stay inside fp16's normal range (about 6e-5 .. 65504); with
+ * fp32 io a token-recurrent fp32 kernel runs instead.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS,
  * GDN_ERR_CKPT, GDN_ERR_HIP.  init_state may alias final_state. */
 GDN_API gdn_status gdn_prefill_packed(const gdn_shape* shape, const int32_t* cu_seqlens,
