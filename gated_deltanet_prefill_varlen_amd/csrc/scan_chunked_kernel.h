@@ -157,8 +157,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, b2));
 }
 
-// Row of accumulator register i for lane half g.
-__device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
 
 template <int DK, int DV>
 struct Cfg {
