@@ -164,9 +164,9 @@ struct Cfg {
   static constexpr int NW = DV / 32;      // waves
   static constexpr int NTH = 64 * NW;     // threads
   static constexpr int KT = DK / 32;      // 32-wide k tiles of the state
-  static constexpr int LDK = DK + 4;      // row stride of sK, sQ (fp16; 8-byte aligned rows)
+  static constexpr int LDK = DK + 12;     // row stride of sK, sQ (fp16; 8-byte aligned rows)
   static constexpr int LDT = CT + 4;      // row stride of sT, sP (fp16)
-  static constexpr int LDV = DV + 8;      // row stride of the V / O tile (bf16; 16-byte rows)
+  static constexpr int LDV = DV + 24;     // row stride of the V / O tile (bf16; 16-byte rows)
   static constexpr int LDA = CT + 4;      // row stride of sA, A transposed (fp32)
   // With four waves, waves 2 and 3 run the substitution while waves 0 and 1
   // form their K S0^T and Q S0^T (waves 2 and 3 formed theirs during the
