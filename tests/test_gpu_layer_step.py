@@ -1,0 +1,84 @@
+"""The whole hot path in the launch configuration the benchmark times, at the
+chat wave's full size: the packed conv1d + SiLU from the pre-conv rows into
+one [T, conv_dim] tensor (conv states, conv windows at the checkpoints), the
+scan reading q, k, v as column views of it, and the checkpoint copy into a
+device pool on its own stream after an event.  Checked against the oracle's
+conv followed by its token-by-token recurrence on sampled (prompt, head)
+pairs (the conv output rounded to bf16 as the tensor stores it), with the
+conv states, windows and pool contents bit-exact (they are copies).
+
+Tolerances: as the prefill tests (states 1e-3 relative Frobenius, bf16
+outputs 2e-2 max-relative per row)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_prefill_varlen_amd as gdn
+import oracle as O
+import workloads as W
+from gpu_util import DEV, STATE_TOL, OUT_TOL, io_tensor, f32_tensor, i32_tensor, sample_pairs, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def test_layer_step_chat_wave_sampled():
+    p = W.chat_wave(seed=0, with_conv=True)
+    T, N, Hqk, Hv, d = p.n_tokens, p.n_seqs, p.Hqk, p.Hv, p.dk
+    C = 2 * Hqk * d + Hv * d
+    ck = gdn.gdn_plan_checkpoints(p.cu_seqlens, p.block)
+    n_ck = len(ck)
+    x = io_tensor(p.x, "bf16")
+    w = f32_tensor(p.conv_w)
+    y = torch.empty_like(x)
+    conv_state = torch.empty((N, 3, C), dtype=torch.bfloat16, device=DEV)
+    conv_ckpt = torch.empty((n_ck, 3, C), dtype=torch.bfloat16, device=DEV)
+    cu_d, ck_d = i32_tensor(p.cu_seqlens), i32_tensor(ck)
+    out = torch.empty((T, Hv, d), dtype=torch.bfloat16, device=DEV)
+    final = torch.empty((N, Hv, d, d), dtype=torch.float32, device=DEV)
+    ckbuf = torch.empty((n_ck, Hv, d, d), dtype=torch.float32, device=DEV)
+    pool = torch.zeros((n_ck + 7, Hv, d, d), dtype=torch.float32, device=DEV)
+    slots = np.random.default_rng(3).permutation(n_ck + 7)[:n_ck].astype(np.int64)
+    shape = gdn.make_shape(Hqk, Hv, d, d, p.chunk, q_tok_stride=C, k_tok_stride=C, v_tok_stride=C)
+    stream, cstream = torch.cuda.Stream(), torch.cuda.Stream()
+    scan_done, copy_done = torch.cuda.Event(), torch.cuda.Event()
+    gdn.gdn_conv1d_silu_packed(shape, cu_d, p.cu_seqlens, x, w, y, None, conv_state, ck_d, ck, conv_ckpt,
+                               stream=stream)
+    gdn.gdn_prefill_packed(shape, cu_d, p.cu_seqlens, y[:, :Hqk * d], y[:, Hqk * d:2 * Hqk * d],
+                           y[:, 2 * Hqk * d:], f32_tensor(p.g), f32_tensor(p.beta), None, ck_d, ck, out,
+                           final, ckbuf, stream=stream)
+    scan_done.record(stream)
+    gdn.gdn_snapshot_copy(ckbuf, n_ck, Hv * d * d * 4, pool, torch.from_numpy(slots).to(DEV), slots,
+                          n_ck + 7, wait_event=scan_done, copy_stream=cstream, done_event=copy_done)
+    copy_done.synchronize()
+    torch.cuda.synchronize()
+
+    assert torch.equal(pool[torch.from_numpy(slots).to(DEV)], ckbuf)
+    xb = torch.from_numpy(np.ascontiguousarray(p.x)).view(torch.bfloat16)
+    cu = p.cu_seqlens
+    for s in range(N):   # conv states: each prompt's last three inputs, copies of x
+        assert torch.equal(conv_state[s].cpu(), xb[int(cu[s + 1]) - 3:int(cu[s + 1])])
+    for i, c in enumerate(ck):   # conv windows: the three inputs before each checkpoint
+        assert torch.equal(conv_ckpt[i].cpu(), xb[int(c) - 3:int(c)])
+
+    worst_o = worst_s = 0.0
+    for s, h in sample_pairs(p, 6, seed=5):
+        j = h // (Hv // Hqk)
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        chans = np.r_[j * d:(j + 1) * d, Hqk * d + j * d:Hqk * d + (j + 1) * d,
+                      2 * Hqk * d + h * d:2 * Hqk * d + (h + 1) * d]
+        xs = O.to_f64(p.x[c0:c1][:, chans], "bf16")
+        ys = O.round_bf16(O.conv1d_silu_packed(xs, p.conv_w[chans].astype(np.float64), [0, c1 - c0])[0])
+        q, k, v = ys[:, None, :d], ys[:, None, d:2 * d], ys[:, None, 2 * d:]
+        mine = [int(c) - c0 for c in ck if c0 < c <= c1]
+        ro, rf, rc = O.prefill_recurrent(q, k, v, p.g[c0:c1, h:h + 1].astype(np.float64),
+                                         p.beta[c0:c1, h:h + 1].astype(np.float64), [0, c1 - c0],
+                                         ckpt_positions=mine)
+        eo = float(np.max(O.max_rel_rows(to_f64(out[c0:c1, h]), ro[:, 0])))
+        es = float(O.rel_frobenius(to_f64(final[s, h]), rf[0, 0]))
+        idx = [i for i, c in enumerate(ck) if c0 < c <= c1]
+        for n, i in enumerate(idx):
+            es = max(es, float(O.rel_frobenius(to_f64(ckbuf[i, h]), rc[n, 0])))
+        assert eo <= OUT_TOL["bf16"], f"output rel err {eo:.3e} at seq {s} head {h}"
+        assert es <= STATE_TOL, f"state rel err {es:.3e} at seq {s} head {h}"
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+    print(f"layer step: out {worst_o:.2e} state {worst_s:.2e}")
