@@ -370,6 +370,13 @@ chunked_prefill_kernel(const ScanArgs a) {
         X = mma(kx, sh, X);
         QS = mma(sh, qx, QS);
       }
+    // S0 has served both products: the chunk's decay e^{G_C} goes on here,
+    // in the slack of this wave's stage, rather than in the state path
+    const float gC = exp2f_hw(sG[CT - 1]);
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[kt][i] *= gC;
   };
 
   // Gram-type tile: sum over k of (row c of xa) (row c of xb), the A operand
@@ -687,12 +694,8 @@ chunked_prefill_kernel(const ScanArgs a) {
       if constexpr (PRE)
 #pragma unroll
         for (int ks = 0; ks < DK / 16; ++ks) kta[ks] = ldt(ks / 2, ks % 2);
-      // S = e^{G_C} S + K^T (r_k e^{G_C - G} U); K^T rows by transpose reads
-      const float gC = exp2f_hw(sG[CT - 1]);
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) S[kt][i] *= gC;
+      // S = e^{G_C} S0 + K^T (r_k e^{G_C - G} U), S already decayed after X
+      // and QS; K^T rows by transpose reads
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const float4 c4 = *reinterpret_cast<const float4*>(sCu + 8 * q4 + 4 * g);
