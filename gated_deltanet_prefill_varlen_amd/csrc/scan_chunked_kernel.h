@@ -660,6 +660,15 @@ chunked_prefill_kernel(const ScanArgs a) {
         for (int r = 0; r < 4; ++r) X[4 * q4 + r] = bb[r] * (vv[4 * q4 + r] - kk[r] * X[4 * q4 + r]);
       }
       const f16x8 pA[2] = {lds_op(pr), lds_op(pr + 16)};
+      f16x8 kta[NKS];
+      auto ldt = [&](int kt, int h2) {   // K^T rows 32 kt + c, tokens as in lds_op
+        const uint16_t* p = ktr + 16 * h2 * LDK + 32 * kt;
+        const u32x2 lo = lds_tr4(p), hi = lds_tr4(p + 8 * LDK);
+        return __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      };
+      if constexpr (PRE)
+#pragma unroll
+        for (int ks = 0; ks < DK / 16; ++ks) kta[ks] = ldt(ks / 2, ks % 2);
       // product of a 32x32 LDS block (operands a: columns 0..15, then
       // 16..31) with an accumulator tile
       auto tri_mm = [&](const f16x8 (&ao)[2], const f32x16& y, f32x16 acc) {
@@ -685,15 +694,6 @@ chunked_prefill_kernel(const ScanArgs a) {
       for (int q4 = 0; q4 < 4; ++q4)
         *reinterpret_cast<u32x2*>(sV + c * LDV + 32 * wave + 8 * q4 + 4 * g) =
             u32x2{pack_bf16(QS[4 * q4], QS[4 * q4 + 1]), pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3])};
-      f16x8 kta[NKS];
-      auto ldt = [&](int kt, int h2) {   // K^T rows 32 kt + c, tokens as in lds_op
-        const uint16_t* p = ktr + 16 * h2 * LDK + 32 * kt;
-        const u32x2 lo = lds_tr4(p), hi = lds_tr4(p + 8 * LDK);
-        return __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-      };
-      if constexpr (PRE)
-#pragma unroll
-        for (int ks = 0; ks < DK / 16; ++ks) kta[ks] = ldt(ks / 2, ks % 2);
       // S = e^{G_C} S0 + K^T (r_k e^{G_C - G} U), S already decayed after X
       // and QS; K^T rows by transpose reads
 #pragma unroll
