@@ -626,8 +626,8 @@ chunked_prefill_kernel(const ScanArgs a) {
     {
       // the LDS operands of the stage are requested ahead of their use, so the
       // LDS round trips overlap: V of this wave's columns first, then the T
-      // and P row operands, the K^T row operands of the update (with several
-      // waves) once O is out.  V comes by four transpose reads of the
+      // and P row operands and (with several waves) the K^T operands of the
+      // update.  V comes by four transpose reads of the
       // row-major V tile (as the K^T operands do): lane (c, g) gets column v
       // of rows 8 q4 + 4 g .. +3, the accumulator rows of registers 4q4..4q4+3.
       const uint16_t* tr = sT + c * LDT + 4 * g;
