@@ -187,14 +187,23 @@ def conv_alg_bytes(T: int, N: int, C: int, n_ckpt: int, e: int = 2) -> int:
     return 2 * T * C * e + C * 4 * 4 + (N + n_ckpt) * 3 * C * e
 
 
-def bench_layer_step(torch, gdn, p, steps, warmup, stream, flush, label):
-    """One pass of the whole hot path over the chat wave: the packed conv1d +
-    SiLU from the pre-conv rows x into one [T, conv_dim] tensor (with the
-    prompts' conv states and the conv windows at the checkpoints), the scan
-    reading q, k, v as column views of it (checkpoints into a device buffer),
-    then the checkpoint copy into a device pool on its own stream after an
-    event, joined back before the step's closing event.  Events around the
-    scan launch give the scan kernel's own time for its roofline."""
+def bench_layer_step(torch, gdn, p, steps, warmup, stream, label):
+    """One step is one pass of the whole hot path over the chat wave: the
+    packed conv1d + SiLU from the pre-conv rows x into one [T, conv_dim]
+    tensor (with the prompts' conv states and the conv windows at the
+    checkpoints), the scan reading q, k, v as column views of it (checkpoints
+    into a device buffer, final states), and the copy of those checkpoints
+    into a device pool.  Steps run as a model's consecutive layers would:
+    each step's copy goes on a copy stream right after its scan (an event
+    from the scan), so it reads the checkpoints while the memory-side cache
+    still holds them and runs beside the next step's conv; two checkpoint
+    buffers alternate, and a scan waits for the copy that last read its
+    buffer (the copy of two steps before).  The timed region is the K steps
+    queued back to back between two device synchronisations, the last step's
+    copy joined before its closing event.  Inside it only the scan carries
+    events (its own time, for its roofline); a second region of K steps with
+    events around each conv as well gives the breakdown (each event pair
+    costs a few microseconds, so that region is not the headline)."""
     T, N = p.n_tokens, p.n_seqs
     C = 2 * p.Hqk * p.dk + p.Hv * p.dv
     ck = gdn.gdn_plan_checkpoints(p.cu_seqlens, p.block)
@@ -209,7 +218,7 @@ def bench_layer_step(torch, gdn, p, steps, warmup, stream, flush, label):
     qv, kv, vv = y[:, :p.Hqk * p.dk], y[:, p.Hqk * p.dk:2 * p.Hqk * p.dk], y[:, 2 * p.Hqk * p.dk:]
     out = torch.empty((T, p.Hv, p.dv), dtype=x.dtype, device="cuda:0")
     final = torch.empty((N, p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
-    ckbuf = torch.empty((n_ck, p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
+    ckbufs = [torch.empty((n_ck, p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0") for _ in range(2)]
     pool_slots = n_ck + 32
     pool = torch.empty((pool_slots, p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
     slots = np.random.default_rng(0).permutation(pool_slots)[:n_ck].astype(np.int64)
@@ -219,52 +228,68 @@ def bench_layer_step(torch, gdn, p, steps, warmup, stream, flush, label):
                            gdn.GDN_BF16 if p.dtype == "bf16" else gdn.GDN_F32, scale=p.scale,
                            q_tok_stride=C, k_tok_stride=C, v_tok_stride=C)
     cstream = torch.cuda.Stream()
-    scan_done, copy_done = torch.cuda.Event(), torch.cuda.Event()
+    scan_done = [torch.cuda.Event(), torch.cuda.Event()]
+    copy_done = [torch.cuda.Event(), torch.cuda.Event()]
 
-    def step(ev=None):
-        gdn.gdn_conv1d_silu_packed(shape, cu_d, p.cu_seqlens, x, w, y, None, conv_state, ck_d, ck,
-                                   conv_ckpt, stream=stream)
-        if ev:
-            ev[0].record(stream)
-        gdn.gdn_prefill_packed(shape, cu_d, p.cu_seqlens, qv, kv, vv, g, beta, None, ck_d, ck,
-                               out, final, ckbuf, stream=stream)
-        if ev:
-            ev[1].record(stream)
-        scan_done.record(stream)
-        gdn.gdn_snapshot_copy(ckbuf, n_ck, each, pool, slots_d, slots, pool_slots, wait_event=scan_done,
-                              copy_stream=cstream, done_event=copy_done)
-        stream.wait_event(copy_done)
+    def run(n, rec=None, conv_events=False):
+        for i in range(n):
+            b = i % 2
+            e = rec[i] if rec else None
+            if e and conv_events:
+                e[0].record(stream)
+            gdn.gdn_conv1d_silu_packed(shape, cu_d, p.cu_seqlens, x, w, y, None, conv_state, ck_d, ck,
+                                       conv_ckpt, stream=stream)
+            if e and conv_events:
+                e[1].record(stream)
+            stream.wait_event(copy_done[b])     # the copy that last read this buffer
+            if e:
+                e[2].record(stream)
+            gdn.gdn_prefill_packed(shape, cu_d, p.cu_seqlens, qv, kv, vv, g, beta, None, ck_d, ck,
+                                   out, final, ckbufs[b], stream=stream)
+            if e:
+                e[3].record(stream)
+            scan_done[b].record(stream)
+            gdn.gdn_snapshot_copy(ckbufs[b], n_ck, each, pool, slots_d, slots, pool_slots,
+                                  wait_event=scan_done[b], copy_stream=cstream, done_event=copy_done[b])
+        stream.wait_event(copy_done[(n - 1) % 2])
+
+    def region(conv_events):
+        rec = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        run(steps, rec, conv_events)
+        end.record(stream)
+        end.synchronize()
+        torch.cuda.synchronize()
+        return rec, start.elapsed_time(end), (time.perf_counter() - t0) * 1e3
 
     with torch.cuda.stream(stream):
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        evs = []
-        for _ in range(steps):
-            flush()
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            e[0].record(stream)
-            step(e[1:3])
-            e[3].record(stream)
-            evs.append(e)
-        evs[-1][3].synchronize()
-    torch.cuda.synchronize()
-    step_ms = [a.elapsed_time(d) for a, b, c, d in evs]
-    scan_ms = [b.elapsed_time(c) for a, b, c, d in evs]
-    conv_ms = [a.elapsed_time(b) for a, b, c, d in evs]
-    med = statistics.median(step_ms)
+        run(warmup)
+        rec, region_ms, wall_ms = region(False)
+        rec_b, region_b_ms, _ = region(True)
+    per_step = region_ms / steps
+    spacing = [rec[i][2].elapsed_time(rec[i + 1][2]) for i in range(steps - 1)]
+    scan_ms = [c.elapsed_time(d) for a, b, c, d in rec]
+    conv_ms = [a.elapsed_time(b) for a, b, c, d in rec_b]
+    scan_b_ms = [c.elapsed_time(d) for a, b, c, d in rec_b]
     B_scan = prefill_alg_bytes(p, n_ck, p.init is not None)
     B_conv = conv_alg_bytes(T, N, C, n_ck)
     B_copy = 2 * n_ck * each
     F = prefill_alg_flops(p)
-    exact = bool(torch.equal(pool[slots_d], ckbuf))
+    exact = bool(torch.equal(pool[slots_d], ckbufs[(steps - 1) % 2]) and torch.equal(ckbufs[0], ckbufs[1]))
     return {
         "workload": label, "tokens": T, "prompts": N, "checkpoints": int(n_ck),
-        "ms_median": med, "ms_mean": statistics.fmean(step_ms),
-        "ms_p10": float(np.percentile(step_ms, 10)), "ms_p90": float(np.percentile(step_ms, 90)),
-        "tokens_per_s": T / (med * 1e-3),
-        "conv_ms_median": statistics.median(conv_ms),
+        "ms_per_step": per_step, "region_ms": region_ms, "region_wall_ms": wall_ms,
+        "tokens_per_s": T / (per_step * 1e-3),
+        "step_spacing_ms_median": statistics.median(spacing) if spacing else per_step,
+        "step_spacing_ms_p10": float(np.percentile(spacing, 10)) if spacing else per_step,
+        "step_spacing_ms_p90": float(np.percentile(spacing, 90)) if spacing else per_step,
         "scan_ms_median": statistics.median(scan_ms), "scan_ms_mean": statistics.fmean(scan_ms),
+        "breakdown_region": {"ms_per_step": region_b_ms / steps,
+                             "conv_ms_median": statistics.median(conv_ms),
+                             "scan_ms_median": statistics.median(scan_b_ms)},
         "scan_alg_bytes": B_scan, "scan_alg_flops": F,
         "step_alg_bytes": B_scan + B_conv + B_copy,
         "copy_exact": exact,
@@ -585,9 +610,10 @@ def main():
     if args.workload == "chat":
         log("[bench] timing headline step (conv, scan, checkpoint copy)")
         label += ": conv1d+SiLU, scan with checkpoints, checkpoint copy on its own stream"
-        step = bench_layer_step(torch, gdn, p, args.steps, args.warmup, stream, flush, label)
-        head = {"workload": label, "ms_median": step["ms_median"], "tokens_per_s": step["tokens_per_s"],
-                "ms_p10": step["ms_p10"], "ms_p90": step["ms_p90"], "checkpoints": step["checkpoints"],
+        step = bench_layer_step(torch, gdn, p, args.steps, args.warmup, stream, label)
+        head = {"workload": label, "ms_median": step["ms_per_step"], "tokens_per_s": step["tokens_per_s"],
+                "ms_p10": step["step_spacing_ms_p10"], "ms_p90": step["step_spacing_ms_p90"],
+                "checkpoints": step["checkpoints"],
                 "alg_bytes": step["scan_alg_bytes"], "alg_flops": step["scan_alg_flops"],
                 "scan_ms_mean": step["scan_ms_mean"], "step": step}
     else:
@@ -643,9 +669,13 @@ def main():
         "config": {"workload": head["workload"], "tokens": p.n_tokens, "prompts": p.n_seqs,
                    "qk_heads": p.Hqk, "v_heads": p.Hv, "head_dim": p.dk, "chunk": p.chunk,
                    "checkpoint_block": p.block, "checkpoints": head["checkpoints"],
-                   "timing": "median of per-step HIP-event times on the launch stream (the copy "
-                             "stream joined before the closing event); 1 GiB cache flush before "
-                             "each step, outside the events",
+                   "timing": ("K steps queued back to back between two device synchronisations, "
+                              "each step's checkpoint copy on its own stream right after its scan, "
+                              "beside the next step's conv, the last copy joined; ms_per_step = "
+                              "HIP-event time of the "
+                              "region / K" if args.workload == "chat" else
+                              "median of per-launch HIP-event times on the launch stream; 1 GiB "
+                              "cache flush before each launch, outside the events"),
                    "wall_s_timed_region": t_wall},
         "step": head.get("step"),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,

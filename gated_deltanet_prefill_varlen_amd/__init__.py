@@ -149,6 +149,17 @@ def _event(ev) -> Optional[int]:
     return int(ev) or None
 
 
+def _record_target(ev) -> Optional[int]:
+    """Handle of an event the library records.  torch makes an event's HIP
+    handle only at its first record, and a null handle would leave the event
+    unrecorded (a later wait on it would not wait), so a fresh torch event is
+    recorded once on the current stream first; the library's own record after
+    its work is the one every later wait sees."""
+    if isinstance(ev, torch.cuda.Event) and not ev.cuda_event:
+        ev.record()
+    return _event(ev)
+
+
 def _check(status: int, where: str) -> None:
     if status != 0:
         raise GdnError(status, where)
@@ -224,9 +235,11 @@ def gdn_conv1d_silu_packed(shape: gdn_shape, cu_seqlens, cu_seqlens_host, x, wei
 def gdn_snapshot_copy(ckpt_buf, n: int, bytes_each: int, dst_pool, dst_slot, dst_slot_host,
                       pool_slots: int, wait_event=None, copy_stream=None, done_event=None) -> None:
     """Copy n checkpoint items of bytes_each bytes into pool slots.  dst_pool is
-    a device tensor, or an int device address of mapped pinned host memory."""
+    a device tensor, or an int device address of mapped pinned host memory.
+    copy_stream first waits for wait_event; done_event is recorded on
+    copy_stream after the copy."""
     sl_h = _host_i64(dst_slot_host)
     dst = dst_pool if isinstance(dst_pool, int) else _dev(dst_pool)
     _check(load().gdn_snapshot_copy(
         _dev(ckpt_buf), int(n), int(bytes_each), dst, int(pool_slots), _dev(dst_slot), _hp(sl_h),
-        _event(wait_event), _stream(copy_stream), _event(done_event)), "gdn_snapshot_copy")
+        _event(wait_event), _stream(copy_stream), _record_target(done_event)), "gdn_snapshot_copy")

@@ -212,6 +212,7 @@ def test_snapshot_copy_device_pool_on_own_stream():
     done = torch.cuda.Event()
     gdn.gdn_snapshot_copy(dp.ckpt_buf, n, each, pool, torch.from_numpy(slots).to(DEV), slots, n + 7,
                           wait_event=scan_done, copy_stream=copy_stream, done_event=done)
+    assert done.cuda_event, "the copy-done event was left unrecorded"
     done.synchronize()
     assert torch.equal(pool[torch.from_numpy(slots).to(DEV)], dp.ckpt_buf)
     rest = np.setdiff1d(np.arange(n + 7), slots)

@@ -2,10 +2,13 @@
 chat wave's full size: the packed conv1d + SiLU from the pre-conv rows into
 one [T, conv_dim] tensor (conv states, conv windows at the checkpoints), the
 scan reading q, k, v as column views of it, and the checkpoint copy into a
-device pool on its own stream after an event.  Checked against the oracle's
-conv followed by its token-by-token recurrence on sampled (prompt, head)
-pairs (the conv output rounded to bf16 as the tensor stores it), with the
-conv states, windows and pool contents bit-exact (they are copies).
+device pool on its own stream.  Two steps run as consecutive layers: each
+step's copy waits for an event from its scan and runs beside the next step's
+work, the two steps writing alternate checkpoint buffers (the second with
+other gates, so that a copy of the wrong buffer shows).  The second step is checked against the oracle's conv followed by
+its token-by-token recurrence on sampled (prompt, head) pairs (the conv
+output rounded to bf16 as the tensor stores it); conv states, windows and
+both pools are bit-exact (they are copies).
 
 Tolerances: as the prefill tests (states 1e-3 relative Frobenius, bf16
 outputs 2e-2 max-relative per row)."""
@@ -35,24 +38,38 @@ def test_layer_step_chat_wave_sampled():
     cu_d, ck_d = i32_tensor(p.cu_seqlens), i32_tensor(ck)
     out = torch.empty((T, Hv, d), dtype=torch.bfloat16, device=DEV)
     final = torch.empty((N, Hv, d, d), dtype=torch.float32, device=DEV)
-    ckbuf = torch.empty((n_ck, Hv, d, d), dtype=torch.float32, device=DEV)
-    pool = torch.zeros((n_ck + 7, Hv, d, d), dtype=torch.float32, device=DEV)
+    ckbufs = [torch.empty((n_ck, Hv, d, d), dtype=torch.float32, device=DEV) for _ in range(2)]
+    pools = [torch.zeros((n_ck + 7, Hv, d, d), dtype=torch.float32, device=DEV) for _ in range(2)]
     slots = np.random.default_rng(3).permutation(n_ck + 7)[:n_ck].astype(np.int64)
+    slots_d = torch.from_numpy(slots).to(DEV)
     shape = gdn.make_shape(Hqk, Hv, d, d, p.chunk, q_tok_stride=C, k_tok_stride=C, v_tok_stride=C)
     stream, cstream = torch.cuda.Stream(), torch.cuda.Stream()
-    scan_done, copy_done = torch.cuda.Event(), torch.cuda.Event()
-    gdn.gdn_conv1d_silu_packed(shape, cu_d, p.cu_seqlens, x, w, y, None, conv_state, ck_d, ck, conv_ckpt,
-                               stream=stream)
-    gdn.gdn_prefill_packed(shape, cu_d, p.cu_seqlens, y[:, :Hqk * d], y[:, Hqk * d:2 * Hqk * d],
-                           y[:, 2 * Hqk * d:], f32_tensor(p.g), f32_tensor(p.beta), None, ck_d, ck, out,
-                           final, ckbuf, stream=stream)
-    scan_done.record(stream)
-    gdn.gdn_snapshot_copy(ckbuf, n_ck, Hv * d * d * 4, pool, torch.from_numpy(slots).to(DEV), slots,
-                          n_ck + 7, wait_event=scan_done, copy_stream=cstream, done_event=copy_done)
-    copy_done.synchronize()
+    scan_done = [torch.cuda.Event(), torch.cuda.Event()]
+    copy_done = [torch.cuda.Event(), torch.cuda.Event()]
+    other = W.chat_wave(seed=1)
+    gates = [(f32_tensor(p.g), f32_tensor(p.beta)), (f32_tensor(other.g), f32_tensor(other.beta))]
+
+    def copy(b):
+        gdn.gdn_snapshot_copy(ckbufs[b], n_ck, Hv * d * d * 4, pools[b], slots_d, slots, n_ck + 7,
+                              wait_event=scan_done[b], copy_stream=cstream, done_event=copy_done[b])
+
+    for b in range(2):
+        gdn.gdn_conv1d_silu_packed(shape, cu_d, p.cu_seqlens, x, w, y, None, conv_state, ck_d, ck,
+                                   conv_ckpt, stream=stream)
+        gdn.gdn_prefill_packed(shape, cu_d, p.cu_seqlens, y[:, :Hqk * d], y[:, Hqk * d:2 * Hqk * d],
+                               y[:, 2 * Hqk * d:], gates[b][0], gates[b][1], None, ck_d, ck, out,
+                               final, ckbufs[b], stream=stream)
+        scan_done[b].record(stream)
+        copy(b)                            # beside the next step's conv
+    stream.wait_event(copy_done[1])
+    assert copy_done[0].cuda_event and copy_done[1].cuda_event, "copy-done events left unrecorded"
     torch.cuda.synchronize()
 
-    assert torch.equal(pool[torch.from_numpy(slots).to(DEV)], ckbuf)
+    for b in range(2):
+        assert torch.equal(pools[b][slots_d], ckbufs[b])
+    assert not torch.equal(ckbufs[0], ckbufs[1])
+    ckbuf = ckbufs[1]
+    g_np, beta_np = other.g, other.beta
     xb = torch.from_numpy(np.ascontiguousarray(p.x)).view(torch.bfloat16)
     cu = p.cu_seqlens
     for s in range(N):   # conv states: each prompt's last three inputs, copies of x
@@ -70,8 +87,8 @@ def test_layer_step_chat_wave_sampled():
         ys = O.round_bf16(O.conv1d_silu_packed(xs, p.conv_w[chans].astype(np.float64), [0, c1 - c0])[0])
         q, k, v = ys[:, None, :d], ys[:, None, d:2 * d], ys[:, None, 2 * d:]
         mine = [int(c) - c0 for c in ck if c0 < c <= c1]
-        ro, rf, rc = O.prefill_recurrent(q, k, v, p.g[c0:c1, h:h + 1].astype(np.float64),
-                                         p.beta[c0:c1, h:h + 1].astype(np.float64), [0, c1 - c0],
+        ro, rf, rc = O.prefill_recurrent(q, k, v, g_np[c0:c1, h:h + 1].astype(np.float64),
+                                         beta_np[c0:c1, h:h + 1].astype(np.float64), [0, c1 - c0],
                                          ckpt_positions=mine)
         eo = float(np.max(O.max_rel_rows(to_f64(out[c0:c1, h]), ro[:, 0])))
         es = float(O.rel_frobenius(to_f64(final[s, h]), rf[0, 0]))

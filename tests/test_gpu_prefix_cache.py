@@ -60,6 +60,7 @@ def test_restore_from_pinned_pool_continues_bitwise(dk, dv):
     done = torch.cuda.Event()
     gdn.gdn_snapshot_copy(dp.ckpt_buf, n, each, _device_address(pool), torch.from_numpy(slots).to(DEV),
                           slots, n + 5, wait_event=scan_done, copy_stream=copy_stream, done_event=done)
+    assert done.cuda_event, "the copy-done event was left unrecorded"
     done.synchronize()
     ckpt_host = dp.ckpt_buf.cpu()
     assert torch.equal(pool[torch.from_numpy(slots)], ckpt_host)
