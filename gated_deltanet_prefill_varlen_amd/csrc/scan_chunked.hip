@@ -9,12 +9,14 @@ namespace chunked {
 hipError_t launch_dk32(const ScanArgs& a, hipStream_t st);
 hipError_t launch_dk64(const ScanArgs& a, hipStream_t st);
 hipError_t launch_dk128(const ScanArgs& a, hipStream_t st);
+hipError_t launch_pipe_dk128(const ScanArgs& a, hipStream_t st);
 }  // namespace chunked
 
 hipError_t launch_prefill(const ScanArgs& a, hipStream_t st) {
   if (!a.bf16) return launch_prefill_recurrent(a, st);
   if (a.dk == 32) return chunked::launch_dk32(a, st);
   if (a.dk == 64) return chunked::launch_dk64(a, st);
+  if (a.dk == 128 && a.dv == 128 && a.chunk >= 32) return chunked::launch_pipe_dk128(a, st);
   if (a.dk == 128) return chunked::launch_dk128(a, st);
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,497 @@
+// Chunked gated-delta-rule prefill with the chunk's work pipelined over wave
+// roles (d_k = d_v = 128, 32-token chunks, bf16 io).
+//
+// Per chunk the arithmetic is that of chunked_prefill_kernel
+// (scan_chunked_kernel.h: the WY/UT form of Yang et al., NeurIPS 2024, gated
+// as in Gated Delta Networks, ICLR 2025; fp16 MFMA operands, fp32
+// accumulation and state).  The work split differs: one workgroup of eight
+// waves per (prompt, value head), one workgroup per CU.
+//   - state waves 0..3 each own 32 state columns in MFMA accumulators for the
+//     whole prompt and run the state path of chunk c (X = K S0^T, Q S0^T, the
+//     decay, Y, U = T Y, the output rows, the state update, checkpoints);
+//   - in the same barrier interval the preparation waves 4..7 stage chunk
+//     c+3, waves 4 and 5 form
+//     the Gram and K Q^T tiles of chunk c+2 with the per-token factors, and
+//     waves 6 and 7 invert the (I + A) block of chunk c+1.
+// Only the state path depends on the state; the rest of a chunk's work runs
+// three intervals ahead of it, beside it on the same SIMDs, and each chunk
+// costs one barrier.  A ring of four LDS slots (K, Q, V/O and P tiles and the
+// per-token scalars) carries a chunk from its staging to its state path (the
+// state waves store their output rows straight from registers); A
+// and T are double-buffered.  A prompt of n chunks takes n + 3 intervals
+// (rounded up to even).  The two roles run separate loops with the same
+// barrier count: the state waves keep the state in their registers, the
+// preparation waves keep two chunks' rows in flight in theirs, loaded two
+// intervals ahead of their staging.
+#pragma once
+
+#include "scan_chunked_kernel.h"
+
+namespace gdn {
+namespace chunked {
+
+template <int DK, int DV>
+struct PipeCfg {
+  static constexpr int CT = 32;                 // tokens per chunk
+  static constexpr int NSW = DV / 32;           // state waves
+  static constexpr int NPW = 4;                 // preparation waves
+  static constexpr int P0 = 64 * NSW;           // first preparation thread
+  static constexpr int PTH = 64 * NPW;          // preparation threads
+  static constexpr int NTH = P0 + PTH;
+  static constexpr int KT = DK / 32;
+  static constexpr int LDK = DK + 12;           // row strides as in Cfg
+  static constexpr int LDT = CT + 4;
+  static constexpr int LDV = DV + 24;
+  static constexpr int LDA = CT + 4;
+  static constexpr int LPC = 4, MPL = CT / LPC; // substitution: 4 lanes per column of T
+  static constexpr int SUB0 = 2 * 64;           // first substitution thread (preparation index)
+  static constexpr int RING = 4;
+  static constexpr int kScal = 12;
+  static constexpr int rK = 0;                  // ring slot layout
+  static constexpr int rQ = rK + CT * LDK * 2;
+  static constexpr int rV = rQ + CT * LDK * 2;  // V tile
+  static constexpr int rP = rV + CT * LDV * 2;
+  static constexpr int rS = rP + CT * LDT * 2;
+  static constexpr int SLOT = rS + kScal * CT * 4;
+  static constexpr int oA = RING * SLOT;        // two A tiles (fp32, transposed)
+  static constexpr int oT = oA + 2 * CT * LDA * 4;   // two T tiles (fp16)
+  static constexpr int bytes = oT + 2 * CT * LDT * 2;
+  static constexpr int NVV = CT * DV / 8 / PTH; // 16-byte V/O pieces per preparation thread
+  static_assert(NSW == 4 && DK == 128, "laid out for d_k = d_v = 128");
+  static_assert(CT * DK / 16 == PTH && NVV * PTH == CT * DV / 8, "staging shares");
+  static_assert(SUB0 + CT * LPC == PTH, "waves 6 and 7 substitute");
+  static_assert(bytes <= 160 * 1024, "LDS of one CU");
+  static_assert(SLOT % 16 == 0 && rQ % 16 == 0 && rV % 16 == 0 && rP % 16 == 0 && rS % 16 == 0 &&
+                oA % 16 == 0 && oT % 16 == 0, "align");
+};
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(64 * (DV / 32 + 4), 1)
+pipelined_prefill_kernel(const ScanArgs a) {
+  using C = PipeCfg<DK, DV>;
+  constexpr int CT = C::CT, KT = C::KT, LDK = C::LDK, LDT = C::LDT, LDA = C::LDA, LDV = C::LDV;
+  constexpr int LPC = C::LPC, MPL = C::MPL, NSW = C::NSW, PTH = C::PTH;
+  constexpr int NKS = DK / 16;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int s = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31, g = lane >> 5;
+  const int grp = lane >> 4, li = lane & 15;
+  const int ptid = tid - C::P0;   // preparation thread index (negative in the state waves)
+  const int j = h / (a.Hv / a.Hqk);
+  const int seq0 = a.cu[s], seq1 = a.cu[s + 1];
+  const int nch = (seq1 - seq0 + CT - 1) / CT;
+  auto rows_of = [&](int ch) { return min(CT, seq1 - seq0 - ch * CT); };
+
+  auto slot = [&](int ch) { return smem + (ch & (C::RING - 1)) * C::SLOT; };
+  auto ringK = [&](int ch) { return reinterpret_cast<uint16_t*>(slot(ch) + C::rK); };
+  auto ringQ = [&](int ch) { return reinterpret_cast<uint16_t*>(slot(ch) + C::rQ); };
+  auto ringV = [&](int ch) { return reinterpret_cast<uint16_t*>(slot(ch) + C::rV); };
+  auto ringP = [&](int ch) { return reinterpret_cast<uint16_t*>(slot(ch) + C::rP); };
+  auto ringSc = [&](int ch) { return reinterpret_cast<float*>(slot(ch) + C::rS); };
+  auto bufA = [&](int ch) { return reinterpret_cast<float*>(smem + C::oA + (ch & 1) * (CT * LDA * 4)); };
+  auto bufT = [&](int ch) { return reinterpret_cast<uint16_t*>(smem + C::oT + (ch & 1) * (CT * LDT * 2)); };
+
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k);
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)h * DV;
+  uint16_t* og = static_cast<uint16_t*>(a.out) + (size_t)h * DV;
+  const size_t sstride = (size_t)a.Hv * DV * DK;
+  const int v = 32 * (wave & (NSW - 1)) + c;   // a state wave's column (value dim)
+  // transpose-read bases (as in chunked_prefill_kernel): lanes of 16-lane
+  // group grp cover columns 16 (grp % 2) .. +15 and rows 4 (grp / 2) + j of
+  // a tile; lane 4j + r names the 4-column piece r of row j
+  const int ktr = (4 * (grp >> 1) + (li >> 2)) * LDK + 16 * (grp & 1) + 4 * (li & 3);
+  const int vtr = (4 * (grp >> 1) + (li >> 2)) * LDV + 32 * (wave & (NSW - 1)) + 16 * (grp & 1) + 4 * (li & 3);
+
+  // ---- state slice S^T[k][v] (state waves)
+  f32x16 S[KT];
+  {
+    const float* src = (wave < NSW && a.init) ? a.init + (size_t)s * sstride + ((size_t)h * DV + v) * DK
+                                              : nullptr;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (src) x = *reinterpret_cast<const float4*>(src + 32 * kt + 8 * q4 + 4 * g);
+        S[kt][4 * q4 + 0] = x.x; S[kt][4 * q4 + 1] = x.y;
+        S[kt][4 * q4 + 2] = x.z; S[kt][4 * q4 + 3] = x.w;
+      }
+  }
+  auto store_state = [&](float* dst) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(dst + 32 * kt + 8 * q4 + 4 * g) =
+            make_float4(S[kt][4 * q4], S[kt][4 * q4 + 1], S[kt][4 * q4 + 2], S[kt][4 * q4 + 3]);
+  };
+
+  // checkpoint cursor (state waves), uniform; positions by scalar loads
+  typedef const int32_t __attribute__((address_space(4)))* ConstI32;
+  const ConstI32 ckp = (ConstI32)a.ckpt;
+  int ci = __builtin_amdgcn_readfirstlane(lower_bound_i32(a.ckpt, a.n_ckpt, seq0 + 1));
+  int next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
+
+  // ---- a chunk's HBM rows into registers (preparation waves), as in
+  //      chunked_prefill_kernel: clamped row indices, 32-bit row offsets
+  const uint32_t ksb = (uint32_t)a.k_stride * 2, qsb = (uint32_t)a.q_stride * 2;
+  const uint32_t vsb = (uint32_t)a.v_stride * 2, hv = (uint32_t)a.Hv;
+  auto row = [](const void* base, uint32_t off) { return static_cast<const char*>(base) + off; };
+  // The preparation waves hold two chunks' rows in flight in registers,
+  // loaded two intervals ahead of their staging (an HBM round trip is longer
+  // than an interval): rows of chunk c go to set c % 2.  Each role runs its
+  // own loop, so the two sets are live only in the preparation waves' loop
+  // and the wait before a staging covers only its own set's loads.
+  // K and Q come as row pieces of 16 key dims: preparation thread e holds
+  // dims 16 (e % 8) .. +15 of row e / 8, so a row's squares are summed over
+  // 8 lanes
+  struct Rows {
+    u32x4 k[2], q[2];   // K and Q row pieces (2 x 8 bf16 each)
+    u32x4 v[C::NVV];    // 16-byte V row pieces
+    float g, b;         // log-gate and beta of token `lane`
+  };
+  auto fetch = [&](Rows& R, int ch) {
+    const int t0x = seq0 + ch * CT, nx = rows_of(ch);
+    {
+      const uint32_t t = min(ptid / 8, nx - 1), pb = 32 * (ptid % 8);
+      const uint16_t* kb = kg + (size_t)t0x * a.k_stride + (size_t)j * DK;
+      const uint16_t* qb = qg + (size_t)t0x * a.q_stride + (size_t)j * DK;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        R.k[hh] = *reinterpret_cast<const u32x4*>(row(kb, __umul24(t, ksb) + pb + 16 * hh));
+        R.q[hh] = *reinterpret_cast<const u32x4*>(row(qb, __umul24(t, qsb) + pb + 16 * hh));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < C::NVV; ++u) {
+      const int e = ptid + u * PTH;
+      const uint32_t t = min(e / (DV / 8), nx - 1), c8 = (e % (DV / 8)) * 8;
+      R.v[u] = *reinterpret_cast<const u32x4*>(row(vg + (size_t)t0x * a.v_stride, __umul24(t, vsb) + 2 * c8));
+    }
+    const uint32_t tl = min(lane, nx - 1);
+    R.g = a.g[(size_t)t0x * a.Hv + h + __umul24(tl, hv)];
+    R.b = a.beta[(size_t)t0x * a.Hv + h + __umul24(tl, hv)];
+  };
+
+  // Gram-type tile of two row-major fp16 tiles (row operands read first)
+  auto rows_mm = [&](const uint16_t* xa, const uint16_t* xb) {
+    f16x8 ar[NKS], br[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      ar[ks] = lds_op(xa + c * LDK + 4 * g + 16 * ks);
+      br[ks] = lds_op(xb + c * LDK + 4 * g + 16 * ks);
+    }
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) acc = mma(ar[ks], br[ks], acc);
+    return acc;
+  };
+
+  // the preparation waves' part of interval it; R holds the rows of chunk it
+  // and takes those of chunk it + 2
+  auto prep = [&](Rows& R, int it) {
+    // ======== preparation waves ========
+    // -- staging of chunk it into its ring slot
+    const int cs = it;
+    if (cs < nch) {
+      const int n = rows_of(cs);
+      uint16_t* sK = ringK(cs);
+      uint16_t* sQ = ringQ(cs);
+      float* sc = ringSc(cs);
+      const int t = ptid / 8, pc = ptid % 8;   // row, 16-dim piece
+      u32x4 kx[2] = {R.k[0], R.k[1]}, qx[2] = {R.q[0], R.q[1]};
+      if (t >= n) {   // a prompt's last chunk: rows past n are zeros
+        kx[0] = kx[1] = qx[0] = qx[1] = u32x4{0u, 0u, 0u, 0u};
+      }
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          float s1, s2;
+          const u32x2 kf = bf16x4_to_f16(u32x2{kx[hh][2 * w2], kx[hh][2 * w2 + 1]}, s1);
+          const u32x2 qf = bf16x4_to_f16(u32x2{qx[hh][2 * w2], qx[hh][2 * w2 + 1]}, s2);
+          sk += s1;
+          sq += s2;
+          *reinterpret_cast<u32x2*>(sK + t * LDK + 16 * pc + 8 * hh + 4 * w2) = kf;
+          *reinterpret_cast<u32x2*>(sQ + t * LDK + 16 * pc + 8 * hh + 4 * w2) = qf;
+        }
+      sk = group_sum<8>(sk);
+      sq = group_sum<8>(sq);
+      if (pc == 7) {   // zero-padded rows keep r = 1
+        const bool nrm = a.l2norm && t < n;
+        sc[SC_RK * CT + t] = nrm ? __builtin_amdgcn_rsqf(sk + a.eps) : 1.0f;
+        sc[SC_RQ * CT + t] = nrm ? __builtin_amdgcn_rsqf(sq + a.eps) : 1.0f;
+      }
+      if (wave == NSW) {   // betas and the base-2 cumsum of the log-gates
+        const float xg = scan32(lane < n ? R.g : 0.f) * 1.44269504088896341f;
+        if (lane < CT) {
+          sc[SC_G * CT + lane] = xg;
+          sc[SC_BETA * CT + lane] = lane < n ? R.b : 0.f;
+        }
+      }
+    }
+    if (cs < nch) {
+      const int n = rows_of(cs);
+      uint16_t* sV = ringV(cs);
+#pragma unroll
+      for (int u = 0; u < C::NVV; ++u) {
+        const int e = ptid + u * PTH;
+        const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+        *reinterpret_cast<u32x4*>(sV + t * LDV + c8) = t < n ? R.v[u] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    // -- the rows of chunk it + 2 into R (past the last chunk the last
+    //    chunk's rows again: the loads stay unconditional, so the wait for a
+    //    set never has to assume the other set was not issued)
+    fetch(R, min(cs + 2, nch - 1));
+
+    const int cg = it - 1;
+    if (cg >= 0 && cg < nch) {
+      const uint16_t* sK = ringK(cg);
+      float* sc = ringSc(cg);
+      if (wave == NSW) {
+        // A[t][i] = beta_t r_t r_i e^{G_t - G_i} k_t.k_i (i < t), stored
+        // transposed with rows interleaved over the substitution's lane parts
+        float* sA = bufA(cg);
+        if (lane < CT) {
+          const float G = sc[SC_G * CT + lane], lr = __builtin_amdgcn_logf(sc[SC_RK * CT + lane]);
+          sc[SC_LA * CT + lane] = G + (__builtin_amdgcn_logf(sc[SC_BETA * CT + lane]) + lr);
+          sc[SC_LK0 * CT + lane] = G - lr;
+        }
+        const f32x16 acc = rows_mm(sK, sK);
+        const float lki = sc[SC_LK0 * CT + c];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int tb = 8 * q4 + 4 * g;
+          const float4 L4 = *reinterpret_cast<const float4*>(sc + SC_LA * CT + tb);
+          const float La[4] = {L4.x, L4.y, L4.z, L4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = tb + r;
+            const float f = exp2f_hw(La[r] - lki) * acc[4 * q4 + r];
+            sA[c * LDA + (t % LPC) * MPL + MPL - 1 - t / LPC] = c < t ? f : 0.f;
+          }
+        }
+        if (lane < CT) {
+          const float G = sc[SC_G * CT + lane], GC = sc[SC_G * CT + CT - 1];
+          const float rk = sc[SC_RK * CT + lane];
+          sc[SC_CK * CT + lane] = rk * exp2f_hw(G);
+          sc[SC_CQ * CT + lane] = a.scale * sc[SC_RQ * CT + lane] * exp2f_hw(G);
+          sc[SC_CU * CT + lane] = rk * exp2f_hw(GC - G);
+        }
+      } else if (wave == NSW + 1) {
+        // P[t][i] = scale r_q,t r_k,i e^{G_t - G_i} q_t.k_i (i <= t), row t fp16
+        uint16_t* sP = ringP(cg);
+        if (lane < CT) {
+          const float G = sc[SC_G * CT + lane];
+          sc[SC_LQ * CT + lane] = G + __builtin_amdgcn_logf(sc[SC_RQ * CT + lane]);
+          sc[SC_LK1 * CT + lane] = G - __builtin_amdgcn_logf(sc[SC_RK * CT + lane]);
+        }
+        const f32x16 acc = rows_mm(sK, ringQ(cg));
+        const float lqt = sc[SC_LQ * CT + c];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ib = 8 * q4 + 4 * g;
+          const float4 L4 = *reinterpret_cast<const float4*>(sc + SC_LK1 * CT + ib);
+          const float Lk[4] = {L4.x, L4.y, L4.z, L4.w};
+          float pv4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float f = a.scale * exp2f_hw(lqt - Lk[r]) * acc[4 * q4 + r];
+            pv4[r] = ib + r <= c ? f : 0.f;
+          }
+          *reinterpret_cast<u32x2*>(sP + c * LDT + ib) =
+              u32x2{pack_f16(pv4[0], pv4[1]), pack_f16(pv4[2], pv4[3])};
+        }
+      }
+    }
+
+    // -- T = (I + A)^-1 of chunk it - 2 (waves 6, 7): right-looking forward
+    //    substitution as in chunked_prefill_kernel, LPC lanes per column
+    const int cb = it - 2;
+    if (cb >= 0 && cb < nch && ptid >= C::SUB0) {
+      const int st = ptid - C::SUB0;
+      const int jj = st / LPC, q = st % LPC;
+      const float* ab = bufA(cb) + q * MPL;
+      float Tl[MPL];
+#pragma unroll
+      for (int m = 0; m < MPL; ++m) Tl[m] = (q + LPC * m == jj) ? 1.f : 0.f;
+      constexpr int SB = 4, NB = CT / SB;
+      float col[2][SB][MPL];
+      auto load_batch = [&](float (&dst)[SB][MPL], int bt) {
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+#pragma unroll
+          for (int p4 = 0; p4 < MPL; p4 += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(ab + (SB * bt + u) * LDA + p4);
+            dst[u][MPL - 1 - p4] = x.x; dst[u][MPL - 2 - p4] = x.y;
+            dst[u][MPL - 3 - p4] = x.z; dst[u][MPL - 4 - p4] = x.w;
+          }
+      };
+      load_batch(col[0], 0);
+#pragma unroll
+      for (int bt = 0; bt < NB; ++bt) {
+        if (bt + 1 < NB) load_batch(col[(bt + 1) & 1], bt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int t = SB * bt + u;
+          if (t < CT - 1) {
+            const float own = Tl[t / LPC];
+            const int qt = t % LPC;
+            const float Tt = qt == 0 ? group_bcast<LPC, 0>(own)
+                           : qt == 1 ? group_bcast<LPC, 1>(own)
+                           : qt == 2 ? group_bcast<LPC, 2>(own) : group_bcast<LPC, 3>(own);
+#pragma unroll
+            for (int m = t / LPC; m < MPL; ++m) Tl[m] = fmaf(-col[bt & 1][u][m], Tt, Tl[m]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      uint16_t* tcol = bufT(cb) + jj;
+#pragma unroll
+      for (int m = 0; m < MPL; ++m) tcol[(q + LPC * m) * LDT] = f16_bits(Tl[m]);
+    }
+      };
+
+  // intervals: nch + 3, rounded up to even so that the preparation loop
+  // runs both of its halves on every trip (the extra interval is empty)
+  const int nint = (nch + 4) & ~1;
+  if (wave < NSW) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the state loads drained before the loop
+    for (int it = 0; it < nint; ++it) {
+      // ======== state path of chunk it - 3 ========
+      const int cx = it - 3;
+      if (cx >= 0 && cx < nch) {
+        const int n = rows_of(cx);
+        const uint16_t* sK = ringK(cx);
+        const uint16_t* sQ = ringQ(cx);
+        uint16_t* sV = ringV(cx);
+        const float* sc = ringSc(cx);
+        const float* sBeta = sc + SC_BETA * CT;
+        const float* sCk = sc + SC_CK * CT;
+        const float* sCq = sc + SC_CQ * CT;
+        const float* sCu = sc + SC_CU * CT;
+        // X = K S0^T and QS = S0 Q^T for this wave's columns (S0 rounded to
+        // fp16 per k tile), then the chunk's decay on S
+        f32x16 X = {}, QS = {};
+        {
+          f16x8 ka[NKS], qa[NKS];
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            ka[ks] = lds_op(sK + c * LDK + 4 * g + 16 * ks);
+            qa[ks] = lds_op(sQ + c * LDK + 4 * g + 16 * ks);
+          }
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const f16x8 sh = h2 == 0 ? acc_half<0>(S[kt]) : acc_half<1>(S[kt]);
+              X = mma(ka[2 * kt + h2], sh, X);
+              QS = mma(sh, qa[2 * kt + h2], QS);
+            }
+          const float gC = exp2f_hw(sc[SC_G * CT + CT - 1]);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) S[kt][i] *= gC;
+        }
+        // V of this wave's columns by transpose reads, then the T and P row
+        // operands and the K^T operands of the update, requested ahead
+        const uint16_t* tr = bufT(cx) + c * LDT + 4 * g;
+        const uint16_t* pr = ringP(cx) + c * LDT + 4 * g;
+        float vv[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const u32x2 w = lds_tr4(sV + vtr + 8 * q4 * LDV);
+          vv[4 * q4] = __uint_as_float(w.x << 16);
+          vv[4 * q4 + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+          vv[4 * q4 + 2] = __uint_as_float(w.y << 16);
+          vv[4 * q4 + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const f16x8 tA[2] = {lds_op(tr), lds_op(tr + 16)};
+        // Y = beta (V - r_k e^G X), in place of X (rows past n: exact zeros)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int tb = 8 * q4 + 4 * g;
+          const float4 b4 = *reinterpret_cast<const float4*>(sBeta + tb);
+          const float4 k4 = *reinterpret_cast<const float4*>(sCk + tb);
+          const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) X[4 * q4 + r] = bb[r] * (vv[4 * q4 + r] - kk[r] * X[4 * q4 + r]);
+        }
+        const f16x8 pA[2] = {lds_op(pr), lds_op(pr + 16)};
+        f16x8 kta[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const uint16_t* p = sK + ktr + 16 * (ks % 2) * LDK + 32 * (ks / 2);
+          const u32x2 lo = lds_tr4(p), hi = lds_tr4(p + 8 * LDK);
+          kta[ks] = __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        }
+        // U = T Y
+        f32x16 U = {};
+        U = mma(tA[0], acc_half<0>(X), U);
+        U = mma(tA[1], acc_half<1>(X), U);
+        // O^T = scale r_q e^G (S0 Q^T) + U^T P^T, token t = c per lane: the
+        // wave's 32 columns of row t go to HBM as four 8-byte bf16 pieces
+        {
+          const float cq = sCq[c];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) QS[i] *= cq;
+        }
+        QS = mma(acc_half<0>(U), pA[0], QS);
+        QS = mma(acc_half<1>(U), pA[1], QS);
+        if (c < n) {
+          uint16_t* orow = og + (size_t)(seq0 + cx * CT + c) * a.Hv * DV + 32 * wave + 4 * g;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<u32x2*>(orow + 8 * q4) =
+                u32x2{pack_bf16(QS[4 * q4], QS[4 * q4 + 1]), pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3])};
+        }
+        // S = (e^{G_C} S0) + K^T (r_k e^{G_C - G} U)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 c4 = *reinterpret_cast<const float4*>(sCu + 8 * q4 + 4 * g);
+          U[4 * q4] *= c4.x; U[4 * q4 + 1] *= c4.y;
+          U[4 * q4 + 2] *= c4.z; U[4 * q4 + 3] *= c4.w;
+        }
+        const f16x8 uh[2] = {acc_half<0>(U), acc_half<1>(U)};
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) S[kt] = mma(kta[2 * kt + h2], uh[h2], S[kt]);
+        const int t_end = seq0 + cx * CT + n;
+        if (t_end == next_ck) {
+          store_state(a.ckpt_buf + (size_t)ci * sstride + ((size_t)h * DV + v) * DK);
+          ci = __builtin_amdgcn_readfirstlane(ci + 1);
+          next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
+        }
+      }
+      __syncthreads();
+    }
+  } else if (nch > 0) {
+    Rows R0, R1;
+    fetch(R0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // chunk 0's loads first: the first staging waits for them alone
+    fetch(R1, min(1, nch - 1));
+    for (int it = 0; it < nint; it += 2) {   // two intervals per trip: R0 even, R1 odd
+      prep(R0, it);
+      __syncthreads();
+      prep(R1, it + 1);
+      __syncthreads();
+    }
+  } else {
+    for (int it = 0; it < nint; ++it) __syncthreads();
+  }
+  if (wave < NSW && a.final_state)
+    store_state(a.final_state + (size_t)s * sstride + ((size_t)h * DV + v) * DK);
+}
+
+}  // namespace chunked
+}  // namespace gdn
