@@ -681,7 +681,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(args.workload),
-                     "kernel": "chunked_prefill_kernel<128,128>", "alg_bytes_per_launch": head["alg_bytes"],
+                     "kernel": "pipelined_prefill_kernel<128,128>", "alg_bytes_per_launch": head["alg_bytes"],
                      "launch_ms_mean": head["scan_ms_mean"],
                      "mfma_alg_tflops": head["alg_flops"] / mean_s / 1e12},
         "cpu_baseline": cpu,
