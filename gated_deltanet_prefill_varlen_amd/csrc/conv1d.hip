@@ -5,6 +5,8 @@
 // every output row written once.  A wave covers 512 consecutive channels of
 // one token, so each row access is a contiguous 1 KiB (bf16) or 2 KiB (fp32)
 // segment.
+#include <climits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -84,12 +86,46 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
+// The three inputs before position e of prompt s (history from its conv
+// state where e - 3 reaches before the prompt), channels c0 .. c0 + 7, to
+// dst[3][conv_dim].  All reads come before any write: safe when dst is the
+// conv state being read.
 template <typename IO>
-__global__ void __launch_bounds__(kThreads) conv_silu_kernel(const ConvArgs a) {
+__device__ __forceinline__ void copy_window(const ConvArgs& a, int s, int e, typename IO::T* dst, int c0) {
+  const int start = a.cu[s];
+  float v[3][kVec];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) load_ext<IO>(a, s, start, e - 3 + j, c0, v[j]);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) store8<IO>(dst + (size_t)j * a.conv_dim + c0, v[j]);
+}
+
+// blockIdx.x: a block of kThreads x kVec channels (the channel blocks of a
+// strip are neighbours in dispatch order, so a strip's rows are read whole);
+// row index b = blockIdx.y + 65535 blockIdx.z: b < n_strips a strip of
+// tokens, then n_ck checkpoint windows, then the conv-state windows (the last
+// three inputs of each prompt) when they are written here.
+template <typename IO>
+__global__ void __launch_bounds__(kThreads) conv_silu_kernel(const ConvArgs a, int n_strips, int n_ck, int n_rows) {
   constexpr int kS = Raw8<IO>::kStrip;
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * kVec;
-  const int p0 = blockIdx.y * kS;
-  if (c0 >= a.conv_dim || p0 >= a.n_tokens) return;
+  const int b = blockIdx.y + 65535 * blockIdx.z;
+  if (c0 >= a.conv_dim || b >= n_rows) return;
+  if (b >= n_strips) {
+    const int i = b - n_strips;
+    if (i < n_ck) {
+      const int e = a.ckpt[i];
+      copy_window<IO>(a, seq_of_token(a.cu, a.n_seqs, e - 1), e,
+                      static_cast<typename IO::T*>(a.conv_ckpt) + (size_t)i * 3 * a.conv_dim, c0);
+    } else {
+      const int sq = i - n_ck;
+      copy_window<IO>(a, sq, a.cu[sq + 1], static_cast<typename IO::T*>(a.state_out) + (size_t)sq * 3 * a.conv_dim,
+                      c0);
+    }
+    return;
+  }
+  const int p0 = b * kS;
+  if (p0 >= a.n_tokens) return;
   const int np = min(kS, a.n_tokens - p0);
   const typename IO::T* xp = static_cast<const typename IO::T*>(a.x);
 
@@ -142,63 +178,41 @@ __global__ void __launch_bounds__(kThreads) conv_silu_kernel(const ConvArgs a) {
   }
 }
 
-// The three inputs before position e of prompt s, copied to dst[3][conv_dim].
-// by_ckpt = 0: e = end of prompt blockIdx.y (conv state out);
-// by_ckpt = 1: e = checkpoint blockIdx.y (its prompt found from cu).
+// Conv states out when they overwrite the conv states in: a launch of its
+// own after the conv (which reads the states in), one block row per prompt.
 template <typename IO>
-__global__ void __launch_bounds__(kThreads) conv_window_kernel(const ConvArgs a, int by_ckpt) {
+__global__ void __launch_bounds__(kThreads) conv_state_kernel(const ConvArgs a) {
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * kVec;
   if (c0 >= a.conv_dim) return;
-  const int i = blockIdx.y;
-  int s, e;
-  typename IO::T* dst;
-  if (by_ckpt) {
-    e = a.ckpt[i];
-    s = seq_of_token(a.cu, a.n_seqs, e - 1);
-    dst = static_cast<typename IO::T*>(a.conv_ckpt) + (size_t)i * 3 * a.conv_dim;
-  } else {
-    s = i;
-    e = a.cu[s + 1];
-    dst = static_cast<typename IO::T*>(a.state_out) + (size_t)i * 3 * a.conv_dim;
-  }
-  const int start = a.cu[s];
-  float v[3][kVec];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) load_ext<IO>(a, s, start, e - 3 + j, c0, v[j]);
-  // all reads above happen before any write: safe when state_out == state_in
-#pragma unroll
-  for (int j = 0; j < 3; ++j) store8<IO>(dst + (size_t)j * a.conv_dim + c0, v[j]);
+  const int sq = blockIdx.y;
+  copy_window<IO>(a, sq, a.cu[sq + 1], static_cast<typename IO::T*>(a.state_out) + (size_t)sq * 3 * a.conv_dim, c0);
 }
 
 template <typename IO>
 hipError_t launch(const ConvArgs& a, hipStream_t st) {
-  const int gx = (a.conv_dim / kVec + kThreads - 1) / kThreads;
-  if (a.n_tokens > 0) {
-    constexpr int kS = Raw8<IO>::kStrip;
-    dim3 grid(gx, (a.n_tokens + kS - 1) / kS);
-    hipLaunchKernelGGL(conv_silu_kernel<IO>, grid, dim3(kThreads), 0, st, a);
+  constexpr int kS = Raw8<IO>::kStrip;
+  const int gc = (a.conv_dim / kVec + kThreads - 1) / kThreads;
+  const int64_t n_strips = (a.n_tokens + kS - 1) / kS;
+  const int64_t n_ck = a.conv_ckpt ? a.n_ckpt : 0;
+  // conv states out in the same launch unless they overwrite the states in
+  // (the conv and the checkpoint windows read those)
+  const bool in_place = a.state_out && a.state_out == a.state_in;
+  const int64_t n_st = a.state_out && !in_place ? a.n_seqs : 0;
+  const int64_t rows = n_strips + n_ck + n_st;
+  if (rows > INT_MAX) return hipErrorInvalidValue;
+  if (rows > 0) {
+    const dim3 grid(gc, (uint32_t)std::min<int64_t>(rows, 65535), (uint32_t)((rows + 65534) / 65535));
+    hipLaunchKernelGGL(conv_silu_kernel<IO>, grid, dim3(kThreads), 0, st, a, (int)n_strips, (int)n_ck, (int)rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // checkpoint windows read the conv state in, so they go before it is overwritten
-  for (int i0 = 0; a.conv_ckpt && i0 < a.n_ckpt; i0 += 65535) {
-    ConvArgs b = a;
-    b.ckpt = a.ckpt + i0;
-    b.conv_ckpt = static_cast<char*>(a.conv_ckpt) + (size_t)i0 * 3 * a.conv_dim * IO::kBytes;
-    hipLaunchKernelGGL(conv_window_kernel<IO>, dim3(gx, min(65535, a.n_ckpt - i0)), dim3(kThreads),
-                       0, st, b, 1);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  for (int s0 = 0; a.state_out && s0 < a.n_seqs; s0 += 65535) {
+  for (int s0 = 0; in_place && s0 < a.n_seqs; s0 += 65535) {
     ConvArgs b = a;
     b.cu = a.cu + s0;
     b.n_seqs = a.n_seqs - s0;
-    if (a.state_in)
-      b.state_in = static_cast<const char*>(a.state_in) + (size_t)s0 * 3 * a.conv_dim * IO::kBytes;
+    b.state_in = static_cast<const char*>(a.state_in) + (size_t)s0 * 3 * a.conv_dim * IO::kBytes;
     b.state_out = static_cast<char*>(a.state_out) + (size_t)s0 * 3 * a.conv_dim * IO::kBytes;
-    hipLaunchKernelGGL(conv_window_kernel<IO>, dim3(gx, min(65535, a.n_seqs - s0)), dim3(kThreads),
-                       0, st, b, 0);
+    hipLaunchKernelGGL(conv_state_kernel<IO>, dim3(gc, min(65535, a.n_seqs - s0)), dim3(kThreads), 0, st, b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
