@@ -172,6 +172,38 @@ def test_conv_in_place_state_and_no_history():
     np.testing.assert_array_equal(to_f64(state), rst)
 
 
+def test_conv_large_pack_past_grid_row_limit():
+    """A pack of 1.1M tokens (68,752 strips of 16 plus the checkpoint windows
+    and conv states, past the 65,535 rows of one grid dimension): sampled rows
+    on both sides of row 65,535 * 16 and at the end against the oracle's conv
+    of that slice (its three history rows passed as the conv state); conv
+    states and checkpoint windows bit-exact (they are copies)."""
+    lens = [600_000, 500_017]
+    T, C = sum(lens), 96                     # Hqk = Hv = 1, d = 32
+    rng = np.random.default_rng(21)
+    xb = W.f32_to_bf16_bits(W._normal(rng, (T, C)))
+    w = (0.5 * W._normal(rng, (C, 4))).astype(np.float32)
+    cu = np.array([0, lens[0], T], dtype=np.int32)
+    ck = gdn.gdn_plan_checkpoints(cu, 4096)
+    x = io_tensor(xb, "bf16")
+    y = torch.empty_like(x)
+    st_out = torch.empty((2, 3, C), dtype=torch.bfloat16, device=DEV)
+    win = torch.empty((len(ck), 3, C), dtype=torch.bfloat16, device=DEV)
+    gdn.gdn_conv1d_silu_packed(gdn.make_shape(1, 1, 32, 32, 64), i32_tensor(cu), cu, x, f32_tensor(w), y,
+                               None, st_out, i32_tensor(ck), ck, win)
+    torch.cuda.synchronize()
+    x64 = O.to_f64(xb, "bf16")
+    for r0, r1 in ((65535 * 16 - 200, 65535 * 16 + 200), (T - 4096, T)):
+        ry, _, _ = O.conv1d_silu_packed(x64[r0:r1], w.astype(np.float64), [0, r1 - r0],
+                                        conv_state=x64[None, r0 - 3:r0])
+        assert np.max(O.max_rel_rows(to_f64(y[r0:r1]), ry)) <= OUT_TOL["bf16"], (r0, r1)
+    xt = torch.from_numpy(np.ascontiguousarray(xb)).view(torch.bfloat16)
+    for s in range(2):
+        assert torch.equal(st_out[s].cpu(), xt[int(cu[s + 1]) - 3:int(cu[s + 1])])
+    for i, c in enumerate(ck):
+        assert torch.equal(win[i].cpu(), xt[int(c) - 3:int(c)])
+
+
 def test_tiny_pipeline_conv_then_scan():
     """Tiny workload end to end: conv on the drawn q|k|v, then the scan with
     its own L2 norm, against the oracle's conv followed by its scan."""
