@@ -4,25 +4,25 @@
 // Per chunk the arithmetic is that of chunked_prefill_kernel
 // (scan_chunked_kernel.h: the WY/UT form of Yang et al., NeurIPS 2024, gated
 // as in Gated Delta Networks, ICLR 2025; fp16 MFMA operands, fp32
-// accumulation and state).  The work split differs: one workgroup of eight
-// waves per (prompt, value head), one workgroup per CU.
+// accumulation and state).  The work split differs: one workgroup of twelve
+// waves per (prompt, value head), one workgroup per CU, three waves per SIMD.
 //   - state waves 0..3 each own 32 state columns in MFMA accumulators for the
 //     whole prompt and run the state path of chunk c (X = K S0^T, Q S0^T, the
 //     decay, Y, U = T Y, the output rows, the state update, checkpoints);
-//   - in the same barrier interval the preparation waves 4..7 stage chunk
-//     c+3, waves 4 and 5 form
-//     the Gram and K Q^T tiles of chunk c+2 with the per-token factors, and
-//     waves 6 and 7 invert the (I + A) block of chunk c+1.
+//   - in the same barrier interval the loader waves 4..7 stage chunk c+3 and
+//     request the rows of chunk c+5, and the factor waves 8..11 form the Gram
+//     and K Q^T tiles of chunk c+2 with the per-token factors (waves 8, 9)
+//     and invert the (I + A) block of chunk c+1 (waves 10, 11).
 // Only the state path depends on the state; the rest of a chunk's work runs
-// three intervals ahead of it, beside it on the same SIMDs, and each chunk
-// costs one barrier.  A ring of four LDS slots (K, Q, V/O and P tiles and the
-// per-token scalars) carries a chunk from its staging to its state path (the
-// state waves store their output rows straight from registers); A
-// and T are double-buffered.  A prompt of n chunks takes n + 3 intervals
-// (rounded up to even).  The two roles run separate loops with the same
-// barrier count: the state waves keep the state in their registers, the
-// preparation waves keep two chunks' rows in flight in theirs, loaded two
-// intervals ahead of their staging.
+// ahead of it on the other waves of the same SIMDs, and each chunk costs one
+// barrier.  A ring of four LDS slots (K, Q, V and P tiles and the per-token
+// scalars) carries a chunk from its staging to its state path (the state
+// waves store their output rows straight from registers); A and T are
+// double-buffered.  A prompt of n chunks takes n + 3 intervals (rounded up
+// to even).  Each role runs its own loop with the same barrier count: the
+// state waves keep the state in their registers, the loader waves two
+// chunks' rows in flight in theirs, loaded two intervals ahead of their
+// staging.
 #pragma once
 
 #include "scan_chunked_kernel.h"
@@ -34,17 +34,19 @@ template <int DK, int DV>
 struct PipeCfg {
   static constexpr int CT = 32;                 // tokens per chunk
   static constexpr int NSW = DV / 32;           // state waves
-  static constexpr int NPW = 4;                 // preparation waves
-  static constexpr int P0 = 64 * NSW;           // first preparation thread
-  static constexpr int PTH = 64 * NPW;          // preparation threads
-  static constexpr int NTH = P0 + PTH;
+  static constexpr int NLW = 4;                 // loader waves (rows in, staging)
+  static constexpr int NFW = 4;                 // factor waves (Gram, K Q^T, substitution)
+  static constexpr int P0 = 64 * NSW;           // first loader thread
+  static constexpr int PTH = 64 * NLW;          // loader threads
+  static constexpr int F0 = P0 + PTH;           // first factor thread
+  static constexpr int NTH = F0 + 64 * NFW;
   static constexpr int KT = DK / 32;
   static constexpr int LDK = DK + 12;           // row strides as in Cfg
   static constexpr int LDT = CT + 4;
   static constexpr int LDV = DV + 24;
   static constexpr int LDA = CT + 4;
   static constexpr int LPC = 4, MPL = CT / LPC; // substitution: 4 lanes per column of T
-  static constexpr int SUB0 = 2 * 64;           // first substitution thread (preparation index)
+  static constexpr int SUB0 = 2 * 64;           // first substitution thread (factor index)
   static constexpr int RING = 4;
   static constexpr int kScal = 12;
   static constexpr int rK = 0;                  // ring slot layout
@@ -59,14 +61,14 @@ struct PipeCfg {
   static constexpr int NVV = CT * DV / 8 / PTH; // 16-byte V/O pieces per preparation thread
   static_assert(NSW == 4 && DK == 128, "laid out for d_k = d_v = 128");
   static_assert(CT * DK / 16 == PTH && NVV * PTH == CT * DV / 8, "staging shares");
-  static_assert(SUB0 + CT * LPC == PTH, "waves 6 and 7 substitute");
+  static_assert(SUB0 + CT * LPC == 64 * NFW, "the last two factor waves substitute");
   static_assert(bytes <= 160 * 1024, "LDS of one CU");
   static_assert(SLOT % 16 == 0 && rQ % 16 == 0 && rV % 16 == 0 && rP % 16 == 0 && rS % 16 == 0 &&
                 oA % 16 == 0 && oT % 16 == 0, "align");
 };
 
 template <int DK, int DV>
-__global__ void __launch_bounds__(64 * (DV / 32 + 4), 1)
+__global__ void __launch_bounds__(64 * (DV / 32 + 8), 1)
 pipelined_prefill_kernel(const ScanArgs a) {
   using C = PipeCfg<DK, DV>;
   constexpr int CT = C::CT, KT = C::KT, LDK = C::LDK, LDT = C::LDT, LDA = C::LDA, LDV = C::LDV;
@@ -193,8 +195,8 @@ pipelined_prefill_kernel(const ScanArgs a) {
 
   // the preparation waves' part of interval it; R holds the rows of chunk it
   // and takes those of chunk it + 2
-  auto prep = [&](Rows& R, int it) {
-    // ======== preparation waves ========
+  auto load_stage = [&](Rows& R, int it) {
+    // ======== loader waves ========
     // -- staging of chunk it into its ring slot
     const int cs = it;
     if (cs < nch) {
@@ -249,12 +251,18 @@ pipelined_prefill_kernel(const ScanArgs a) {
     //    chunk's rows again: the loads stay unconditional, so the wait for a
     //    set never has to assume the other set was not issued)
     fetch(R, min(cs + 2, nch - 1));
+  };
 
+  // the factor waves' part of interval it: Gram and K Q^T tiles of chunk
+  // it - 1 (waves NSW + NLW, + 1), the substitution of chunk it - 2 (the
+  // other two)
+  auto factor = [&](int it) {
+    const int fw = wave - NSW - C::NLW, ftid = tid - C::F0;
     const int cg = it - 1;
     if (cg >= 0 && cg < nch) {
       const uint16_t* sK = ringK(cg);
       float* sc = ringSc(cg);
-      if (wave == NSW) {
+      if (fw == 0) {
         // A[t][i] = beta_t r_t r_i e^{G_t - G_i} k_t.k_i (i < t), stored
         // transposed with rows interleaved over the substitution's lane parts
         float* sA = bufA(cg);
@@ -284,7 +292,7 @@ pipelined_prefill_kernel(const ScanArgs a) {
           sc[SC_CQ * CT + lane] = a.scale * sc[SC_RQ * CT + lane] * exp2f_hw(G);
           sc[SC_CU * CT + lane] = rk * exp2f_hw(GC - G);
         }
-      } else if (wave == NSW + 1) {
+      } else if (fw == 1) {
         // P[t][i] = scale r_q,t r_k,i e^{G_t - G_i} q_t.k_i (i <= t), row t fp16
         uint16_t* sP = ringP(cg);
         if (lane < CT) {
@@ -314,8 +322,8 @@ pipelined_prefill_kernel(const ScanArgs a) {
     // -- T = (I + A)^-1 of chunk it - 2 (waves 6, 7): right-looking forward
     //    substitution as in chunked_prefill_kernel, LPC lanes per column
     const int cb = it - 2;
-    if (cb >= 0 && cb < nch && ptid >= C::SUB0) {
-      const int st = ptid - C::SUB0;
+    if (cb >= 0 && cb < nch && ftid >= C::SUB0) {
+      const int st = ftid - C::SUB0;
       const int jj = st / LPC, q = st % LPC;
       const float* ab = bufA(cb) + q * MPL;
       float Tl[MPL];
@@ -475,15 +483,20 @@ pipelined_prefill_kernel(const ScanArgs a) {
       }
       __syncthreads();
     }
+  } else if (wave >= NSW + C::NLW) {
+    for (int it = 0; it < nint; ++it) {
+      factor(it);
+      __syncthreads();
+    }
   } else if (nch > 0) {
     Rows R0, R1;
     fetch(R0, 0);
     __builtin_amdgcn_sched_barrier(0);   // chunk 0's loads first: the first staging waits for them alone
     fetch(R1, min(1, nch - 1));
     for (int it = 0; it < nint; it += 2) {   // two intervals per trip: R0 even, R1 odd
-      prep(R0, it);
+      load_stage(R0, it);
       __syncthreads();
-      prep(R1, it + 1);
+      load_stage(R1, it + 1);
       __syncthreads();
     }
   } else {
