@@ -18,23 +18,26 @@ namespace {
 
 constexpr int kRows = 32;  // state rows per workgroup
 
-// One token of the recurrence for this lane's 16 state entries.
+// q and k scaled to unit length (this lane's 16 elements; the sums of
+// squares over the row's lanes).
+template <int LPR>
+__device__ __forceinline__ void l2norm_kq(float* kv, float* qv, float eps) {
+  float sk = 0.f, sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { sk = fmaf(kv[i], kv[i], sk); sq = fmaf(qv[i], qv[i], sq); }
+  sk = group_sum<LPR>(sk);
+  sq = group_sum<LPR>(sq);
+  const float rk = __builtin_amdgcn_rsqf(sk + eps), rq = __builtin_amdgcn_rsqf(sq + eps);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { kv[i] *= rk; qv[i] *= rq; }
+}
+
+// One token of the recurrence for one row, this lane's 16 state entries:
 //   S <- alpha S + u k^T,  u = beta (v - alpha S k)   (= alpha S (I - beta k k^T) + beta v k^T)
 // Returns o = S q (already summed over the row's lanes).
 template <int LPR>
-__device__ __forceinline__ float token_step(float* S, float* kv, float* qv, float vrow, float g,
-                                            float beta, int l2norm, float eps) {
-  if (l2norm) {
-    float sk = 0.f, sq = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { sk = fmaf(kv[i], kv[i], sk); sq = fmaf(qv[i], qv[i], sq); }
-    sk = group_sum<LPR>(sk);
-    sq = group_sum<LPR>(sq);
-    const float rk = __builtin_amdgcn_rsqf(sk + eps), rq = __builtin_amdgcn_rsqf(sq + eps);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { kv[i] *= rk; qv[i] *= rq; }
-  }
-  const float alpha = __expf(g);
+__device__ __forceinline__ float row_step(float* S, const float* kv, const float* qv, float vrow, float alpha,
+                                          float beta) {
   float x = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) x = fmaf(S[i], kv[i], x);
@@ -47,6 +50,13 @@ __device__ __forceinline__ float token_step(float* S, float* kv, float* qv, floa
     o = fmaf(S[i], qv[i], o);
   }
   return group_sum<LPR>(o);
+}
+
+template <int LPR>
+__device__ __forceinline__ float token_step(float* S, float* kv, float* qv, float vrow, float g,
+                                            float beta, int l2norm, float eps) {
+  if (l2norm) l2norm_kq<LPR>(kv, qv, eps);
+  return row_step<LPR>(S, kv, qv, vrow, __expf(g), beta);
 }
 
 // The lane's 16 elements of a row (chunks of four at 4 LPR i + 4 j).
@@ -125,34 +135,47 @@ recurrent_prefill_kernel(const ScanArgs a) {
   if (a.final_state) store_row16f<LPR>(a.final_state + (size_t)s * state_stride + head_off, jl, S);
 }
 
-template <int DK, int DV, typename IO>
+// A workgroup holds 32 RPT rows of one (sequence, value head): thread (row
+// group rg, lane part jl) holds its 16 entries of rows rg, rg + 32, ...
+// (RPT rows), so it keeps several state rows in flight and forms k, q and
+// their norms once for them.  Each row's arithmetic is that of token_step.
+template <int DK, int DV, int RPT, typename IO>
 __global__ void __launch_bounds__(kRows * (DK / 16))
 decode_kernel(const DecodeArgs a) {
   constexpr int LPR = DK / 16;
   using T = typename IO::T;
   const int b = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int row = blockIdx.z * kRows + tid / LPR;
+  const int rg = blockIdx.z * kRows * RPT + tid / LPR;
   const int jl = tid % LPR;
   const int j = h / (a.Hv / a.Hqk);
   const int r = a.slot ? a.slot[b] : b;
-  float* sp = a.state + (((size_t)r * a.Hv + h) * DV + row) * DK;
-  float S[16];
-  load_row16f<LPR>(sp, jl, S);
+  float* sp = a.state + ((size_t)r * a.Hv + h) * DV * DK;
+  float S[RPT][16];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) load_row16f<LPR>(sp + (size_t)(rg + kRows * i) * DK, jl, S[i]);
   // the sequence's tokens in order, the state staying in registers; the
   // state after each token to its snapshot when asked for
-  for (int i = 0; i < a.n_tok; ++i) {
-    const size_t t = (size_t)b * a.n_tok + i;
-    float kv[16], qv[16];
+  for (int n = 0; n < a.n_tok; ++n) {
+    const size_t t = (size_t)b * a.n_tok + n;
+    float kv[16], qv[16], vrow[RPT];
     load_row16<LPR, IO>(static_cast<const T*>(a.k) + t * a.k_stride + j * DK, jl, kv);
     load_row16<LPR, IO>(static_cast<const T*>(a.q) + t * a.q_stride + j * DK, jl, qv);
-    const float vrow = load1<IO>(static_cast<const T*>(a.v) + t * a.v_stride + (size_t)h * DV + row);
-    const float o = token_step<LPR>(S, kv, qv, vrow, a.g[t * a.Hv + h], a.beta[t * a.Hv + h],
-                                    a.l2norm, a.eps);
-    if (jl == 0) store1<IO>(static_cast<T*>(a.out) + (t * a.Hv + h) * DV + row, a.scale * o);
-    if (a.snap) store_row16f<LPR>(a.snap + ((t * a.Hv + h) * DV + row) * DK, jl, S);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      vrow[i] = load1<IO>(static_cast<const T*>(a.v) + t * a.v_stride + (size_t)h * DV + rg + kRows * i);
+    if (a.l2norm) l2norm_kq<LPR>(kv, qv, a.eps);
+    const float alpha = __expf(a.g[t * a.Hv + h]), beta = a.beta[t * a.Hv + h];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg + kRows * i;
+      const float o = row_step<LPR>(S[i], kv, qv, vrow[i], alpha, beta);
+      if (jl == 0) store1<IO>(static_cast<T*>(a.out) + (t * a.Hv + h) * DV + row, a.scale * o);
+      if (a.snap) store_row16f<LPR>(a.snap + ((t * a.Hv + h) * DV + row) * DK, jl, S[i]);
+    }
   }
-  store_row16f<LPR>(sp, jl, S);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) store_row16f<LPR>(sp + (size_t)(rg + kRows * i) * DK, jl, S[i]);
 }
 
 template <int DK, int DV, typename IO>
@@ -164,8 +187,17 @@ hipError_t launch_rec_prefill(const ScanArgs& a, hipStream_t st) {
 
 template <int DK, int DV, typename IO>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.batch, a.Hv, DV / kRows);
-  hipLaunchKernelGGL((decode_kernel<DK, DV, IO>), grid, dim3(kRows * (DK / 16)), 0, st, a);
+  // one token: one row per thread (more, smaller workgroups start sooner);
+  // several tokens: up to four rows per thread, the k/q loads and norms of
+  // each token shared by them (decode of 32 x 4 tokens 96 -> 81 us)
+  constexpr int RPT = DV / kRows < 4 ? DV / kRows : 4;
+  if (a.n_tok == 1) {
+    hipLaunchKernelGGL((decode_kernel<DK, DV, 1, IO>), dim3(a.batch, a.Hv, DV / kRows), dim3(kRows * (DK / 16)),
+                       0, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<DK, DV, RPT, IO>), dim3(a.batch, a.Hv, DV / (kRows * RPT)),
+                       dim3(kRows * (DK / 16)), 0, st, a);
+  }
   return hipGetLastError();
 }
 
