@@ -80,6 +80,49 @@ def test_empty_prompts_keep_their_state():
     assert_parity(dp, all_pairs(p))
 
 
+# d_k = d_v = 128 with chunk 32 or 64 runs the pipelined kernel (state,
+# loader and factor waves, up to three chunks ahead); the cases below cover
+# its pipeline fill and drain on short prompts, empty prompts, strided views
+# and GQA ratios.
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_pipelined_every_residue(chunk):
+    """Prompts of every length 1..130 (one to five 32-token chunks, most
+    shorter than the pipeline's depth), checkpoints every `chunk` tokens."""
+    p = W.make_pack("residue_pipe", list(range(1, 131)), 2, 4, 128, 128, chunk, chunk, seed=chunk + 7,
+                    init_std=0.1)
+    dp = DevPack(p, _ckpt(p)).run()
+    torch.cuda.synchronize()
+    eo, es = assert_parity(dp, sample_pairs(p, 60, seed=chunk))
+    print(f"pipelined residues chunk {chunk}: out {eo:.2e} state {es:.2e}")
+
+
+def test_pipelined_empty_prompts_and_strided_views():
+    """Empty prompts keep their state bit for bit; q, k, v as column views of
+    one [T, conv_dim] tensor."""
+    p = W.make_pack("empty_views", [0, 70, 0, 0, 129, 0, 33], 2, 4, 128, 128, 64, 64, seed=13, init_std=0.1)
+    T = p.n_tokens
+    row = np.concatenate([p.q.reshape(T, -1), p.k.reshape(T, -1), p.v.reshape(T, -1)], axis=1)
+    big = io_tensor(row, "bf16")
+    nq = p.Hqk * p.dk
+    dp = DevPack(p, _ckpt(p))
+    dp.q, dp.k, dp.v = big[:, :nq], big[:, nq:2 * nq], big[:, 2 * nq:]
+    cd = row.shape[1]
+    dp.run(shape_of(p, q_tok_stride=cd, k_tok_stride=cd, v_tok_stride=cd))
+    torch.cuda.synchronize()
+    fin = to_f64(dp.final)
+    for s in (0, 2, 3, 5):
+        np.testing.assert_array_equal(fin[s], p.init[s].astype(np.float64))
+    assert_parity(dp, all_pairs(p))
+
+
+@pytest.mark.parametrize("hqk,hv", [(4, 4), (1, 4), (2, 8)])
+def test_pipelined_gqa_ratios(hqk, hv):
+    p = W.make_pack("gqa", [150, 1, 95, 64], hqk, hv, 128, 128, 64, 64, seed=10 * hqk + hv, init_std=0.1)
+    dp = DevPack(p, _ckpt(p)).run()
+    torch.cuda.synchronize()
+    assert_parity(dp, all_pairs(p))
+
+
 def test_zero_init_equals_null_init():
     p = W.make_pack("z", [90, 33], 2, 4, 64, 64, 32, 32, seed=4)
     a = DevPack(p, _ckpt(p)).run()
