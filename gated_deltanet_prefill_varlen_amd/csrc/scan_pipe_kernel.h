@@ -58,7 +58,7 @@ struct PipeCfg {
   static constexpr int oA = RING * SLOT;        // two A tiles (fp32, transposed)
   static constexpr int oT = oA + 2 * CT * LDA * 4;   // two T tiles (fp16)
   static constexpr int bytes = oT + 2 * CT * LDT * 2;
-  static constexpr int NVV = CT * DV / 8 / PTH; // 16-byte V/O pieces per preparation thread
+  static constexpr int NVV = CT * DV / 8 / PTH; // 16-byte V pieces per loader thread
   static_assert(NSW == 4 && DK == 128, "laid out for d_k = d_v = 128");
   static_assert(CT * DK / 16 == PTH && NVV * PTH == CT * DV / 8, "staging shares");
   static_assert(SUB0 + CT * LPC == 64 * NFW, "the last two factor waves substitute");
@@ -81,7 +81,7 @@ pipelined_prefill_kernel(const ScanArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
   const int grp = lane >> 4, li = lane & 15;
-  const int ptid = tid - C::P0;   // preparation thread index (negative in the state waves)
+  const int ptid = tid - C::P0;   // loader thread index (negative in the state waves)
   const int j = h / (a.Hv / a.Hqk);
   const int seq0 = a.cu[s], seq1 = a.cu[s + 1];
   const int nch = (seq1 - seq0 + CT - 1) / CT;
@@ -138,17 +138,17 @@ pipelined_prefill_kernel(const ScanArgs a) {
   int ci = __builtin_amdgcn_readfirstlane(lower_bound_i32(a.ckpt, a.n_ckpt, seq0 + 1));
   int next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
 
-  // ---- a chunk's HBM rows into registers (preparation waves), as in
+  // ---- a chunk's HBM rows into registers (loader waves), as in
   //      chunked_prefill_kernel: clamped row indices, 32-bit row offsets
   const uint32_t ksb = (uint32_t)a.k_stride * 2, qsb = (uint32_t)a.q_stride * 2;
   const uint32_t vsb = (uint32_t)a.v_stride * 2, hv = (uint32_t)a.Hv;
   auto row = [](const void* base, uint32_t off) { return static_cast<const char*>(base) + off; };
-  // The preparation waves hold two chunks' rows in flight in registers,
-  // loaded two intervals ahead of their staging (an HBM round trip is longer
-  // than an interval): rows of chunk c go to set c % 2.  Each role runs its
-  // own loop, so the two sets are live only in the preparation waves' loop
-  // and the wait before a staging covers only its own set's loads.
-  // K and Q come as row pieces of 16 key dims: preparation thread e holds
+  // The loader waves hold two chunks' rows in flight in registers, loaded
+  // two intervals ahead of their staging (an HBM round trip is longer than
+  // an interval): rows of chunk c go to set c % 2.  Each role runs its own
+  // loop, so the two sets are live only in the loader waves' loop and the
+  // wait before a staging covers only its own set's loads.
+  // K and Q come as row pieces of 16 key dims: loader thread e holds
   // dims 16 (e % 8) .. +15 of row e / 8, so a row's squares are summed over
   // 8 lanes
   struct Rows {
@@ -193,8 +193,8 @@ pipelined_prefill_kernel(const ScanArgs a) {
     return acc;
   };
 
-  // the preparation waves' part of interval it; R holds the rows of chunk it
-  // and takes those of chunk it + 2
+  // the loader waves' part of interval it; R holds the rows of chunk it and
+  // takes those of chunk it + 2
   auto load_stage = [&](Rows& R, int it) {
     // ======== loader waves ========
     // -- staging of chunk it into its ring slot
@@ -365,9 +365,9 @@ pipelined_prefill_kernel(const ScanArgs a) {
 #pragma unroll
       for (int m = 0; m < MPL; ++m) tcol[(q + LPC * m) * LDT] = f16_bits(Tl[m]);
     }
-      };
+  };
 
-  // intervals: nch + 3, rounded up to even so that the preparation loop
+  // intervals: nch + 3, rounded up to even so that the loader loop
   // runs both of its halves on every trip (the extra interval is empty)
   const int nint = (nch + 4) & ~1;
   if (wave < NSW) {
