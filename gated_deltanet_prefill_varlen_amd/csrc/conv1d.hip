@@ -2,9 +2,10 @@
 // convolution ahead of q, k, v in Gated Delta Networks' block design), never
 // reading across a prompt boundary.  Memory-bound: every input row is read
 // once per strip of 16 (bf16) or 8 (fp32) tokens, plus a 3-row halo, and
-// every output row written once.  A wave covers 512 consecutive channels of
-// one token, so each row access is a contiguous 1 KiB (bf16) or 2 KiB (fp32)
-// segment.
+// every output row written once.  A wave covers 256 consecutive channels of
+// one token, so each row access is a contiguous 512 B (bf16) or 1 KiB (fp32)
+// segment.  Four channels per thread keep a bf16 strip in 70 VGPRs (7 waves
+// per SIMD), which hides the load latency better than 8 channels at 3 waves.
 #include <climits>
 
 #include "gdn_device.h"
@@ -14,14 +15,14 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVec = 8;     // channels per thread (tokens per thread: Raw8<IO>::kStrip)
+constexpr int kVec = 4;     // channels per thread (tokens per thread: RawRow<IO>::kStrip)
 
 template <typename IO>
 __device__ __forceinline__ void load_hist(const ConvArgs& a, int s, int i, int c0, float* out) {
   if (a.state_in) {
     const typename IO::T* p = static_cast<const typename IO::T*>(a.state_in) +
                               ((size_t)s * 3 + i) * a.conv_dim + c0;
-    load8<IO>(p, out);
+    load4<IO>(p, out);
   } else {
 #pragma unroll
     for (int c = 0; c < kVec; ++c) out[c] = 0.f;
@@ -34,50 +35,42 @@ template <typename IO>
 __device__ __forceinline__ void load_ext(const ConvArgs& a, int s, int start, int pp, int c0,
                                          float* out) {
   if (pp >= start)
-    load8<IO>(static_cast<const typename IO::T*>(a.x) + (size_t)pp * a.x_stride + c0, out);
+    load4<IO>(static_cast<const typename IO::T*>(a.x) + (size_t)pp * a.x_stride + c0, out);
   else
     load_hist<IO>(a, s, pp - start + 3, c0, out);
 }
 
-// Raw 8-channel row segments: the strip's rows are all requested before the
+// Raw 4-channel row segments: the strip's rows are all requested before the
 // first is used, so a thread keeps a whole strip of loads in flight.
-template <typename IO> struct Raw8;
-template <> struct Raw8<IoBf16> {
+template <typename IO> struct RawRow;
+template <> struct RawRow<IoBf16> {
   static constexpr int kStrip = 16;
-  uint4 w;
-  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
+  uint2 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint2*>(p); }
   __device__ __forceinline__ void unpack(float* out) const {
-    const uint32_t r[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __uint_as_float(r[i] << 16);
-      out[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
-    }
+    out[0] = __uint_as_float(w.x << 16);
+    out[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    out[2] = __uint_as_float(w.y << 16);
+    out[3] = __uint_as_float(w.y & 0xFFFF0000u);
   }
-  // 8 values rounded to bf16 (nearest even), two per conversion
+  // 4 values rounded to bf16 (nearest even), two per conversion
   static __device__ __forceinline__ void store(uint16_t* p, const float* v) {
     typedef float f2 __attribute__((ext_vector_type(2)));
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    uint4 o;
+    uint2 o;
     o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[0], v[1]}, b2));
     o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[2], v[3]}, b2));
-    o.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[4], v[5]}, b2));
-    o.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[6], v[7]}, b2));
-    *reinterpret_cast<uint4*>(p) = o;
+    *reinterpret_cast<uint2*>(p) = o;
   }
 };
-template <> struct Raw8<IoF32> {
+template <> struct RawRow<IoF32> {
   static constexpr int kStrip = 8;
-  float4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = reinterpret_cast<const float4*>(p)[0];
-    b = reinterpret_cast<const float4*>(p)[1];
-  }
+  float4 a;
+  __device__ __forceinline__ void load(const float* p) { a = *reinterpret_cast<const float4*>(p); }
   __device__ __forceinline__ void unpack(float* out) const {
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
   }
-  static __device__ __forceinline__ void store(float* p, const float* v) { store8<IoF32>(p, v); }
+  static __device__ __forceinline__ void store(float* p, const float* v) { store4<IoF32>(p, v); }
 };
 
 // silu(x) = x / (1 + e^-x) with the hardware exp and reciprocal (about 1 ulp
@@ -87,7 +80,7 @@ __device__ __forceinline__ float silu(float x) {
 }
 
 // The three inputs before position e of prompt s (history from its conv
-// state where e - 3 reaches before the prompt), channels c0 .. c0 + 7, to
+// state where e - 3 reaches before the prompt), channels c0 .. c0 + 3, to
 // dst[3][conv_dim].  All reads come before any write: safe when dst is the
 // conv state being read.
 template <typename IO>
@@ -97,7 +90,7 @@ __device__ __forceinline__ void copy_window(const ConvArgs& a, int s, int e, typ
 #pragma unroll
   for (int j = 0; j < 3; ++j) load_ext<IO>(a, s, start, e - 3 + j, c0, v[j]);
 #pragma unroll
-  for (int j = 0; j < 3; ++j) store8<IO>(dst + (size_t)j * a.conv_dim + c0, v[j]);
+  for (int j = 0; j < 3; ++j) store4<IO>(dst + (size_t)j * a.conv_dim + c0, v[j]);
 }
 
 // blockIdx.x: a block of kThreads x kVec channels (the channel blocks of a
@@ -107,7 +100,7 @@ __device__ __forceinline__ void copy_window(const ConvArgs& a, int s, int e, typ
 // three inputs of each prompt) when they are written here.
 template <typename IO>
 __global__ void __launch_bounds__(kThreads) conv_silu_kernel(const ConvArgs a, int n_strips, int n_ck, int n_rows) {
-  constexpr int kS = Raw8<IO>::kStrip;
+  constexpr int kS = RawRow<IO>::kStrip;
   const int c0 = (blockIdx.x * kThreads + threadIdx.x) * kVec;
   const int b = blockIdx.y + 65535 * blockIdx.z;
   if (c0 >= a.conv_dim || b >= n_rows) return;
@@ -129,7 +122,7 @@ __global__ void __launch_bounds__(kThreads) conv_silu_kernel(const ConvArgs a, i
   const int np = min(kS, a.n_tokens - p0);
   const typename IO::T* xp = static_cast<const typename IO::T*>(a.x);
 
-  Raw8<IO> raw[kS];
+  RawRow<IO> raw[kS];
 #pragma unroll
   for (int i = 0; i < kS; ++i)
     if (i < np) raw[i].load(xp + (size_t)(p0 + i) * a.x_stride + c0);
@@ -173,7 +166,7 @@ __global__ void __launch_bounds__(kThreads) conv_silu_kernel(const ConvArgs a, i
         win[1][c] = win[2][c];
         win[2][c] = xc[c];
       }
-      Raw8<IO>::store(yp + (size_t)p * a.y_stride + c0, yv);
+      RawRow<IO>::store(yp + (size_t)p * a.y_stride + c0, yv);
     }
   }
 }
@@ -190,7 +183,7 @@ __global__ void __launch_bounds__(kThreads) conv_state_kernel(const ConvArgs a) 
 
 template <typename IO>
 hipError_t launch(const ConvArgs& a, hipStream_t st) {
-  constexpr int kS = Raw8<IO>::kStrip;
+  constexpr int kS = RawRow<IO>::kStrip;
   const int gc = (a.conv_dim / kVec + kThreads - 1) / kThreads;
   const int64_t n_strips = (a.n_tokens + kS - 1) / kS;
   const int64_t n_ck = a.conv_ckpt ? a.n_ckpt : 0;

@@ -21,27 +21,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 struct IoBf16 { using T = uint16_t; static constexpr int kBytes = 2; };
 struct IoF32 { using T = float; static constexpr int kBytes = 4; };
 
-// Load 8 consecutive io elements (16-byte aligned for bf16) as fp32.
+// Load 4 consecutive io elements (8-byte aligned for bf16, 16 for fp32) as fp32.
 template <typename IO>
-__device__ __forceinline__ void load8(const typename IO::T* p, float* out);
-
+__device__ __forceinline__ void load4(const typename IO::T* p, float* out);
 template <>
-__device__ __forceinline__ void load8<IoBf16>(const uint16_t* p, float* out) {
-  const uint4 w = *reinterpret_cast<const uint4*>(p);
-  const uint32_t r[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = __uint_as_float(r[i] << 16);
-    out[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
-  }
+__device__ __forceinline__ void load4<IoBf16>(const uint16_t* p, float* out) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  out[0] = __uint_as_float(w.x << 16);
+  out[1] = __uint_as_float(w.x & 0xFFFF0000u);
+  out[2] = __uint_as_float(w.y << 16);
+  out[3] = __uint_as_float(w.y & 0xFFFF0000u);
 }
-
 template <>
-__device__ __forceinline__ void load8<IoF32>(const float* p, float* out) {
+__device__ __forceinline__ void load4<IoF32>(const float* p, float* out) {
   const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
   out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
 template <typename IO>
@@ -58,22 +52,19 @@ __device__ __forceinline__ void store1<IoBf16>(uint16_t* p, float x) { *p = (uin
 template <>
 __device__ __forceinline__ void store1<IoF32>(float* p, float x) { *p = x; }
 
-// Store 8 fp32 values as 8 consecutive io elements.
+// Store 4 fp32 values as 4 consecutive io elements (bf16: nearest even).
 template <typename IO>
-__device__ __forceinline__ void store8(typename IO::T* p, const float* v);
+__device__ __forceinline__ void store4(typename IO::T* p, const float* v);
 template <>
-__device__ __forceinline__ void store8<IoBf16>(uint16_t* p, const float* v) {
-  uint4 w;
+__device__ __forceinline__ void store4<IoBf16>(uint16_t* p, const float* v) {
+  uint2 w;
   w.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
   w.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-  w.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
-  w.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
-  *reinterpret_cast<uint4*>(p) = w;
+  *reinterpret_cast<uint2*>(p) = w;
 }
 template <>
-__device__ __forceinline__ void store8<IoF32>(float* p, const float* v) {
+__device__ __forceinline__ void store4<IoF32>(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
 // 16 consecutive fp32 values, 16-byte aligned.
