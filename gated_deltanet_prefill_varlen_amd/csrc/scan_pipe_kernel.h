@@ -408,6 +408,10 @@ pipelined_prefill_kernel(const ScanArgs a) {
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) S[kt][i] *= gC;
+          // the decayed state is pinned here: left free, the compiler sinks
+          // the 64 multiplies to just before the update (measured slower)
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) asm volatile("" : "+v"(S[kt]));
         }
         // V of this wave's columns by transpose reads, then the T and P row
         // operands and the K^T operands of the update, requested ahead
@@ -446,22 +450,15 @@ pipelined_prefill_kernel(const ScanArgs a) {
         f32x16 U = {};
         U = mma(tA[0], acc_half<0>(X), U);
         U = mma(tA[1], acc_half<1>(X), U);
-        // O^T = scale r_q e^G (S0 Q^T) + U^T P^T, token t = c per lane: the
-        // wave's 32 columns of row t go to HBM as four 8-byte bf16 pieces
+        // the S0 Q^T part of the output: scale r_q e^G per token
         {
           const float cq = sCq[c];
 #pragma unroll
           for (int i = 0; i < 16; ++i) QS[i] *= cq;
         }
-        QS = mma(acc_half<0>(U), pA[0], QS);
-        QS = mma(acc_half<1>(U), pA[1], QS);
-        if (c < n) {
-          uint16_t* orow = og + (size_t)(seq0 + cx * CT + c) * a.Hv * DV + 32 * wave + 4 * g;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<u32x2*>(orow + 8 * q4) =
-                u32x2{pack_bf16(QS[4 * q4], QS[4 * q4 + 1]), pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3])};
-        }
+        // U's operand halves for the output product, which runs after the
+        // state update (off the recurrence; measured 1-5% faster)
+        const f16x8 uo[2] = {acc_half<0>(U), acc_half<1>(U)};
         // S = (e^{G_C} S0) + K^T (r_k e^{G_C - G} U)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -474,6 +471,17 @@ pipelined_prefill_kernel(const ScanArgs a) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) S[kt] = mma(kta[2 * kt + h2], uh[h2], S[kt]);
+        // O^T = scale r_q e^G (S0 Q^T) + U^T P^T, token t = c per lane: the
+        // wave's 32 columns of row t go to HBM as four 8-byte bf16 pieces
+        QS = mma(uo[0], pA[0], QS);
+        QS = mma(uo[1], pA[1], QS);
+        if (c < n) {
+          uint16_t* orow = og + (size_t)(seq0 + cx * CT + c) * a.Hv * DV + 32 * wave + 4 * g;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<u32x2*>(orow + 8 * q4) =
+                u32x2{pack_bf16(QS[4 * q4], QS[4 * q4 + 1]), pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3])};
+        }
         const int t_end = seq0 + cx * CT + n;
         if (t_end == next_ck) {
           store_state(a.ckpt_buf + (size_t)ci * sstride + ((size_t)h * DV + v) * DK);
