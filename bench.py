@@ -197,8 +197,8 @@ def bench_layer_step(torch, gdn, p, steps, warmup, stream, label):
     each step's copy goes on a copy stream right after its scan (an event
     from the scan), so it reads the checkpoints while the memory-side cache
     still holds them and runs beside the next step's conv; two checkpoint
-    buffers alternate, and a scan waits for the copy that last read its
-    buffer (the copy of two steps before).  The timed region is the K steps
+    buffers alternate, and a step waits, ahead of its conv, for the copy
+    that last read its scan's buffer (the copy of two steps before).  The timed region is the K steps
     queued back to back between two device synchronisations, the last step's
     copy joined before its closing event.  Inside it only the scan carries
     events (its own time, for its roofline); a second region of K steps with
@@ -235,22 +235,26 @@ def bench_layer_step(torch, gdn, p, steps, warmup, stream, label):
         for i in range(n):
             b = i % 2
             e = rec[i] if rec else None
+            # the copy that last read this step's checkpoint buffer (two steps
+            # back; it ran beside the previous conv, so this wait is already
+            # met: placed ahead of the conv it keeps the conv-to-scan edge free
+            # of a cross-stream wait)
+            stream.wait_event(copy_done[b])
             if e and conv_events:
                 e[0].record(stream)
             gdn.gdn_conv1d_silu_packed(shape, cu_d, p.cu_seqlens, x, w, y, None, conv_state, ck_d, ck,
                                        conv_ckpt, stream=stream)
             if e and conv_events:
                 e[1].record(stream)
-            stream.wait_event(copy_done[b])     # the copy that last read this buffer
             if e:
                 e[2].record(stream)
             gdn.gdn_prefill_packed(shape, cu_d, p.cu_seqlens, qv, kv, vv, g, beta, None, ck_d, ck,
                                    out, final, ckbufs[b], stream=stream)
-            if e:
-                e[3].record(stream)
-            scan_done[b].record(stream)
+            # one event marks the scan's end, for its timing and for the copy
+            done = e[3] if e else scan_done[b]
+            done.record(stream)
             gdn.gdn_snapshot_copy(ckbufs[b], n_ck, each, pool, slots_d, slots, pool_slots,
-                                  wait_event=scan_done[b], copy_stream=cstream, done_event=copy_done[b])
+                                  wait_event=done, copy_stream=cstream, done_event=copy_done[b])
         stream.wait_event(copy_done[(n - 1) % 2])
 
     def region(conv_events):
