@@ -149,6 +149,20 @@ decode_kernel(const DecodeArgs a) {
   const int rg = blockIdx.z * kRows * RPT + tid / LPR;
   const int jl = tid % LPR;
   const int j = h / (a.Hv / a.Hqk);
+  // a token's inputs do not depend on the slot: token 0's are requested
+  // before the slot -> state address round trip
+  float kv[16], qv[16], vrow[RPT], galpha, gbeta;
+  auto load_tok = [&](int n) {
+    const size_t t = (size_t)b * a.n_tok + n;
+    load_row16<LPR, IO>(static_cast<const T*>(a.k) + t * a.k_stride + j * DK, jl, kv);
+    load_row16<LPR, IO>(static_cast<const T*>(a.q) + t * a.q_stride + j * DK, jl, qv);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      vrow[i] = load1<IO>(static_cast<const T*>(a.v) + t * a.v_stride + (size_t)h * DV + rg + kRows * i);
+    galpha = a.g[t * a.Hv + h];
+    gbeta = a.beta[t * a.Hv + h];
+  };
+  load_tok(0);
   const int r = a.slot ? a.slot[b] : b;
   float* sp = a.state + ((size_t)r * a.Hv + h) * DV * DK;
   float S[RPT][16];
@@ -158,14 +172,9 @@ decode_kernel(const DecodeArgs a) {
   // state after each token to its snapshot when asked for
   for (int n = 0; n < a.n_tok; ++n) {
     const size_t t = (size_t)b * a.n_tok + n;
-    float kv[16], qv[16], vrow[RPT];
-    load_row16<LPR, IO>(static_cast<const T*>(a.k) + t * a.k_stride + j * DK, jl, kv);
-    load_row16<LPR, IO>(static_cast<const T*>(a.q) + t * a.q_stride + j * DK, jl, qv);
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      vrow[i] = load1<IO>(static_cast<const T*>(a.v) + t * a.v_stride + (size_t)h * DV + rg + kRows * i);
+    if (n > 0) load_tok(n);
     if (a.l2norm) l2norm_kq<LPR>(kv, qv, a.eps);
-    const float alpha = __expf(a.g[t * a.Hv + h]), beta = a.beta[t * a.Hv + h];
+    const float alpha = __expf(galpha), beta = gbeta;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg + kRows * i;
@@ -187,12 +196,14 @@ hipError_t launch_rec_prefill(const ScanArgs& a, hipStream_t st) {
 
 template <int DK, int DV, typename IO>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t st) {
-  // one token: one row per thread (more, smaller workgroups start sooner);
-  // several tokens: up to four rows per thread, the k/q loads and norms of
-  // each token shared by them (decode of 32 x 4 tokens 96 -> 81 us)
+  // one token: two rows per thread (32 x 32 heads: 36 us with one row, 33
+  // with two, 38 with four); several tokens: up to four rows per thread, the
+  // k/q loads and norms of each token shared by them (decode of 32 x 4
+  // tokens 96 -> 81 us)
   constexpr int RPT = DV / kRows < 4 ? DV / kRows : 4;
   if (a.n_tok == 1) {
-    hipLaunchKernelGGL((decode_kernel<DK, DV, 1, IO>), dim3(a.batch, a.Hv, DV / kRows), dim3(kRows * (DK / 16)),
+    constexpr int R1 = DV / kRows < 2 ? DV / kRows : 2;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, R1, IO>), dim3(a.batch, a.Hv, DV / (kRows * R1)), dim3(kRows * (DK / 16)),
                        0, st, a);
   } else {
     hipLaunchKernelGGL((decode_kernel<DK, DV, RPT, IO>), dim3(a.batch, a.Hv, DV / (kRows * RPT)),
