@@ -76,7 +76,21 @@ pipelined_prefill_kernel(const ScanArgs a) {
   constexpr int NKS = DK / 16;
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int s = blockIdx.x, h = blockIdx.y;
+  // (prompt, value head) of this workgroup.  Workgroups go to the eight XCDs
+  // round-robin by linear id, each XCD with its own L2: the G = Hv / Hqk
+  // value heads that read the same q/k rows are given linear ids 8 apart
+  // (same XCD, dispatched together), when the (prompt, qk head) groups come
+  // in whole rounds of eight; otherwise the grid's own order.
+  int s = blockIdx.x, h = blockIdx.y;
+  {
+    const int G = a.Hv / a.Hqk, P = a.n_seqs * a.Hqk;
+    if (P % 8 == 0) {
+      const int L = blockIdx.x + a.n_seqs * blockIdx.y;
+      const int r = L % (8 * G), p = 8 * (L / (8 * G)) + r % 8;
+      s = p % a.n_seqs;
+      h = G * (p / a.n_seqs) + r / 8;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
