@@ -9,8 +9,8 @@ same run as legs: the conv at the same shape, the checkpoint copy on its own
 stream, the decode batch and the mixed pass, and the long-prompt and ragged
 packs.
 
-Prints ONE JSON line on stdout.  ``--gpus N`` with N > 1 exits: this build
-runs on one GPU.
+Prints ONE JSON line on stdout.  ``--gpus N`` with N > 1 exits: the
+benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -586,8 +586,8 @@ def main():
                     help="run only the stream-overlap leg (for a rocprofv3 timeline)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on exactly one GPU (the path shards by value-head groups "
-              "with no exchange; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
+        print("bench.py: one GPU only (the path would shard by value-head groups with no exchange "
+              "between GPUs; multi-GPU runs are not implemented). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
