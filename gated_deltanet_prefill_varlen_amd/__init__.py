@@ -84,9 +84,10 @@ def load() -> ctypes.CDLL:
     lib.gdn_prefill_packed.argtypes = [_SP, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _I32, _P, _P, _P, _P]
     lib.gdn_decode_step.restype = _I32
-    lib.gdn_decode_step.argtypes = [_SP, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P]
+    lib.gdn_decode_step.argtypes = [_SP, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P]
     lib.gdn_decode_tokens.restype = _I32
-    lib.gdn_decode_tokens.argtypes = [_SP, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P]
+    lib.gdn_decode_tokens.argtypes = [_SP, _I32, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
+                                      _P, _P, _P]
     lib.gdn_conv1d_silu_packed.restype = _I32
     lib.gdn_conv1d_silu_packed.argtypes = [_SP, _P, _P, _I32, _I32, _P, _I64, _P, _P, _P, _I64,
                                            _P, _P, _P, _I32, _P, _P]
@@ -199,23 +200,26 @@ def gdn_prefill_packed(shape: gdn_shape, cu_seqlens, cu_seqlens_host, q, k, v, g
 
 
 def gdn_decode_step(shape: gdn_shape, q, k, v, g, beta, state, slot=None, slot_host=None,
-                    out=None, stream=None) -> None:
+                    out=None, conv_w=None, conv_state=None, stream=None) -> None:
+    """One token per sequence; with conv_w and conv_state, q, k, v are the
+    conv's inputs and the slots' conv windows move on by one token."""
     sl_h = _host_i32(slot_host)
     _check(load().gdn_decode_step(
         ctypes.byref(shape), int(q.shape[0]), _dev(q), _dev(k), _dev(v), _dev(g), _dev(beta),
-        _dev(state), int(state.shape[0]), _dev(slot), _hp(sl_h), _dev(out), _stream(stream)),
-        "gdn_decode_step")
+        _dev(state), int(state.shape[0]), _dev(slot), _hp(sl_h), _dev(out), _dev(conv_w),
+        _dev(conv_state), _stream(stream)), "gdn_decode_step")
 
 
 def gdn_decode_tokens(shape: gdn_shape, n_tok: int, q, k, v, g, beta, state, slot=None,
-                      slot_host=None, out=None, snapshots=None, stream=None) -> None:
+                      slot_host=None, out=None, snapshots=None, conv_w=None, conv_state=None,
+                      stream=None) -> None:
     """n_tok tokens per sequence (rows b * n_tok + i), states kept per token."""
     sl_h = _host_i32(slot_host)
     batch = int(q.shape[0]) // int(n_tok)
     _check(load().gdn_decode_tokens(
         ctypes.byref(shape), batch, int(n_tok), _dev(q), _dev(k), _dev(v), _dev(g), _dev(beta),
         _dev(state), int(state.shape[0]), _dev(slot), _hp(sl_h), _dev(out), _dev(snapshots),
-        _stream(stream)), "gdn_decode_tokens")
+        _dev(conv_w), _dev(conv_state), _stream(stream)), "gdn_decode_tokens")
 
 
 def gdn_conv1d_silu_packed(shape: gdn_shape, cu_seqlens, cu_seqlens_host, x, weight, y,

@@ -73,12 +73,6 @@ template <> struct RawRow<IoF32> {
   static __device__ __forceinline__ void store(float* p, const float* v) { store4<IoF32>(p, v); }
 };
 
-// silu(x) = x / (1 + e^-x) with the hardware exp and reciprocal (about 1 ulp
-// each, far below the bf16 output rounding); large |x| saturates to x or -0
-__device__ __forceinline__ float silu(float x) {
-  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-}
-
 // The three inputs before position e of prompt s (history from its conv
 // state where e - 3 reaches before the prompt), channels c0 .. c0 + 3, to
 // dst[3][conv_dim].  All reads come before any write: safe when dst is the
@@ -157,11 +151,7 @@ __global__ void __launch_bounds__(kThreads) conv_silu_kernel(const ConvArgs a, i
       raw[i].unpack(xc);
 #pragma unroll
       for (int c = 0; c < kVec; ++c) {
-        float acc = w[c][0] * win[0][c];
-        acc = fmaf(w[c][1], win[1][c], acc);
-        acc = fmaf(w[c][2], win[2][c], acc);
-        acc = fmaf(w[c][3], xc[c], acc);
-        yv[c] = silu(acc);
+        yv[c] = conv4_silu(w[c][0], w[c][1], w[c][2], w[c][3], win[0][c], win[1][c], win[2][c], xc[c]);
         win[0][c] = win[1][c];
         win[1][c] = win[2][c];
         win[2][c] = xc[c];

@@ -52,10 +52,9 @@ gdn_status check_seqlens(const int32_t* cu, int32_t n_seqs, int32_t n_tokens) {
   return GDN_OK;
 }
 
-// Checkpoints: strictly increasing, each inside a prompt (cu[s] < p <= cu[s+1])
-// on that prompt's chunk grid.
-gdn_status check_ckpts(const int32_t* cu, int32_t n_seqs, const int32_t* pos, int32_t n,
-                       int32_t chunk) {
+// Checkpoints: strictly increasing, each inside a prompt (cu[s] < p <= cu[s+1]).
+// Any position works: the scan also ends a chunk at every checkpoint.
+gdn_status check_ckpts(const int32_t* cu, int32_t n_seqs, const int32_t* pos, int32_t n) {
   if (n < 0) return GDN_ERR_SHAPE;
   if (n == 0) return GDN_OK;
   if (!pos) return GDN_ERR_NULL;
@@ -67,7 +66,6 @@ gdn_status check_ckpts(const int32_t* cu, int32_t n_seqs, const int32_t* pos, in
     // skip empty prompts that end exactly at p-1 ... the owner has cu[s] < p
     while (s < n_seqs && !(cu[s] < p && p <= cu[s + 1])) ++s;
     if (s >= n_seqs) return GDN_ERR_CKPT;
-    if ((p - cu[s]) % chunk != 0) return GDN_ERR_CKPT;
   }
   return GDN_OK;
 }
@@ -92,7 +90,7 @@ const char* gdn_status_string(int32_t status) {
     case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: bad count, stride, alignment or size";
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: head dims, chunk, dtype, flags or head ratio not supported";
     case GDN_ERR_SEQLENS: return "GDN_ERR_SEQLENS: cu_seqlens must start at 0, not decrease and end at n_tokens";
-    case GDN_ERR_CKPT: return "GDN_ERR_CKPT: checkpoints must increase and sit on a prompt's chunk grid";
+    case GDN_ERR_CKPT: return "GDN_ERR_CKPT: checkpoints must increase and each lie inside a prompt";
     case GDN_ERR_CAPACITY: return "GDN_ERR_CAPACITY: output list too short or slot outside the pool";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: a HIP call or kernel launch failed";
     default: return "unknown gdn_status";
@@ -150,7 +148,7 @@ gdn_status gdn_prefill_packed(const gdn_shape* shape, const int32_t* cu_seqlens,
   if (n_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL;
   if (n_ckpt < 0) return GDN_ERR_SHAPE;
   if (n_ckpt > 0 && (!ckpt_positions || !ckpt_positions_host || !ckpt_buf)) return GDN_ERR_NULL;
-  st = check_ckpts(cu_seqlens_host, n_seqs, ckpt_positions_host, n_ckpt, shape->chunk);
+  st = check_ckpts(cu_seqlens_host, n_seqs, ckpt_positions_host, n_ckpt);
   if (st != GDN_OK) return st;
   const int64_t Hqk = shape->num_qk_heads, Hv = shape->num_v_heads;
   const int64_t dk = shape->head_k_dim, dv = shape->head_v_dim;
@@ -180,19 +178,21 @@ gdn_status gdn_prefill_packed(const gdn_shape* shape, const int32_t* cu_seqlens,
 gdn_status gdn_decode_step(const gdn_shape* shape, int32_t batch, const void* q, const void* k,
                            const void* v, const float* g, const float* beta, float* state,
                            int64_t pool_slots, const int32_t* slot, const int32_t* slot_host,
-                           void* out, void* stream) {
+                           void* out, const float* conv_w, void* conv_state, void* stream) {
   return gdn_decode_tokens(shape, batch, 1, q, k, v, g, beta, state, pool_slots, slot, slot_host, out,
-                           nullptr, stream);
+                           nullptr, conv_w, conv_state, stream);
 }
 
 gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t batch, int32_t n_tok, const void* q,
                              const void* k, const void* v, const float* g, const float* beta,
                              float* state, int64_t pool_slots, const int32_t* slot,
-                             const int32_t* slot_host, void* out, float* snapshots, void* stream) {
+                             const int32_t* slot_host, void* out, float* snapshots,
+                             const float* conv_w, void* conv_state, void* stream) {
   gdn_status st = check_shape(shape);
   if (st != GDN_OK) return st;
   if (batch < 0 || pool_slots < 0 || n_tok < 1) return GDN_ERR_SHAPE;
   if ((int64_t)batch * n_tok > INT32_MAX) return GDN_ERR_SHAPE;
+  if (!conv_w != !conv_state) return GDN_ERR_NULL;   // the conv needs both
   if (batch == 0) return GDN_OK;
   if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_NULL;
   if (slot) {
@@ -212,14 +212,17 @@ gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t batch, int32_t n_to
   if ((st = resolve_stride(shape, shape->q_tok_stride, Hqk * dk, &qs)) != GDN_OK) return st;
   if ((st = resolve_stride(shape, shape->k_tok_stride, Hqk * dk, &ks)) != GDN_OK) return st;
   if ((st = resolve_stride(shape, shape->v_tok_stride, Hv * dv, &vs)) != GDN_OK) return st;
-  const void* ptrs[] = {q, k, v, out, state, snapshots};
+  const void* ptrs[] = {q, k, v, out, state, snapshots, conv_w, conv_state};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GDN_ERR_SHAPE;
+  const int64_t conv_dim = 2 * Hqk * dk + Hv * dv;
+  if (conv_w && conv_dim > INT32_MAX / 4) return GDN_ERR_SHAPE;
 
   gdn::DecodeArgs a{};
   a.batch = batch; a.n_tok = n_tok; a.snap = snapshots;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.state = state; a.slot = slot; a.out = out;
+  a.conv_w = conv_w; a.conv_state = conv_state; a.conv_dim = (int32_t)conv_dim;
   a.q_stride = qs; a.k_stride = ks; a.v_stride = vs;
   a.Hqk = (int32_t)Hqk; a.Hv = (int32_t)Hv; a.dk = (int32_t)dk; a.dv = (int32_t)dv;
   a.bf16 = shape->io_dtype == GDN_BF16;
@@ -246,8 +249,7 @@ gdn_status gdn_conv1d_silu_packed(const gdn_shape* shape, const int32_t* cu_seql
   if (n_tokens > 0 && (!x || !y)) return GDN_ERR_NULL;
   if (n_ckpt < 0) return GDN_ERR_SHAPE;
   if (n_ckpt > 0 && conv_ckpt && (!ckpt_positions || !ckpt_positions_host)) return GDN_ERR_NULL;
-  st = check_ckpts(cu_seqlens_host, n_seqs, ckpt_positions_host, conv_ckpt ? n_ckpt : 0,
-                   shape->chunk);
+  st = check_ckpts(cu_seqlens_host, n_seqs, ckpt_positions_host, conv_ckpt ? n_ckpt : 0);
   if (st != GDN_OK) return st;
   const int64_t conv_dim = 2LL * shape->num_qk_heads * shape->head_k_dim +
                            (int64_t)shape->num_v_heads * shape->head_v_dim;

@@ -81,6 +81,24 @@ __device__ __forceinline__ void store16f(float* p, const float* v) {
     reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
 }
 
+// ------------------------------------------------------------- conv --
+// The width-4 causal depthwise conv + SiLU of one channel: w0..w3 the taps
+// (w3 on the current input), x0..x3 the inputs oldest first.  One operation
+// order everywhere it is computed, so every kernel gives the same bits.
+// silu(x) = x / (1 + e^-x) with the hardware exp and reciprocal (about 1 ulp
+// each, below the bf16 output rounding); large |x| saturates to x or -0.
+__device__ __forceinline__ float conv4_silu(float w0, float w1, float w2, float w3, float x0, float x1,
+                                            float x2, float x3) {
+  float acc = w0 * x0;
+  acc = fmaf(w1, x1, acc);
+  acc = fmaf(w2, x2, acc);
+  acc = fmaf(w3, x3, acc);
+  return acc * __builtin_amdgcn_rcpf(1.0f + __expf(-acc));
+}
+
+// fp32 -> bf16 -> fp32 (nearest even), the value a bf16 store would hold.
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
 // ------------------------------------------------------- lane reductions --
 // Lane exchange inside a row of 16 lanes (DPP, no LDS round trip).
 // x read from another lane of its row by DPP control CTRL.  Only in-row

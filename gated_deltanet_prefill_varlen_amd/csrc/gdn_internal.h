@@ -41,6 +41,9 @@ struct DecodeArgs {
   float* state;            // [pool, Hv, dv, dk]
   const int32_t* slot;     // [batch] or nullptr (identity)
   void* out;               // [batch, Hv, dv]
+  const float* conv_w;     // [conv_dim, 4] or nullptr (q, k, v are the conv's outputs)
+  void* conv_state;        // [pool, 3, conv_dim] io, with conv_w
+  int32_t conv_dim;
   int64_t q_stride, k_stride, v_stride;
   int32_t Hqk, Hv, dk, dv;
   int32_t bf16;

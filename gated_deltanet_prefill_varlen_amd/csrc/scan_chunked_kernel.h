@@ -23,13 +23,18 @@
 //
 // Precision: every product runs on fp16 operands with fp32 accumulation.
 // The raw bf16 q/k rows convert to fp16 exactly (fp16 carries three more
-// significand bits; values must lie inside fp16's range, |x| < 65504, and
-// rows keep full accuracy while their norm is at least 2^-10).  Values the
-// kernel computes in fp32 (S0, T, P, Y, U) are rounded to fp16 once per
-// product (2^-11 relative), which holds states to about 4e-4 relative
-// Frobenius against fp64 over thousands of tokens, with or without decay;
-// the state itself is accumulated and carried in fp32.  S must also stay
-// inside fp16's range.
+// significand bits) while a row's sum of squares lies in [kQkLo, kQkHi];
+// a row outside is scaled by a power of two first and its row factor
+// carries the inverse.  Values the kernel computes in fp32 (S0, T, P, Y, U)
+// are rounded to fp16 once per product (2^-11 relative), which holds states
+// to about 4e-4 relative Frobenius against fp64 over thousands of tokens,
+// with or without decay; the state itself is accumulated and carried in
+// fp32, each wave's columns as 2^E S with E chosen per chunk from the
+// largest |S| and |v| (kBand), so both stay well inside fp16's range.
+//
+// Chunks follow ChunkWalk: up to a.chunk tokens from the prompt's first
+// token, cut at every checkpoint, so any checkpoint position works and a
+// run resumed from a checkpoint walks the unbroken run's chunks.
 #pragma once
 
 #include <climits>
@@ -151,6 +156,130 @@ __device__ __forceinline__ float group_bcast(float x) {
 
 __device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
+// ------------------------------------------------- fp16 operand range --
+// fp16 holds normal values from 2^-14 to 65504 with 11 significand bits.
+// Rows of q and k whose sum of squares lies in [kQkLo, kQkHi] convert as
+// they are (exactly, from bf16); a row outside is first scaled by 2^a, a
+// power of two that brings its largest element into [1, 2), and its row
+// factor (1/|x| with the L2 norm, else 1) carries 2^-a, so every product of
+// the scan sees the same value.  The band keeps 1/|x| <= 4, which bounds the
+// update operands r_k e^{G_C - G} U.
+constexpr float kQkLo = 0x1p-4f, kQkHi = 0x1p20f;
+// The state columns of a wave are held as 2^E S: E = 0 while the largest
+// |S| entry and the chunk's largest |v| both have a binary exponent in
+// [-kBand, kBand]; otherwise E brings the larger of the two into [1, 2).
+// E is a function of the unscaled values, so a run resumed from a
+// checkpoint takes the same E as the unbroken run, and scaling by powers of
+// two is exact: results stay bit-identical.
+constexpr int kBand = 6;
+constexpr int kNoExp = -1024;   // exponent of an all-zero set
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Running maxima of bf16 magnitudes: m holds two 16-bit maxima, w two bf16
+// values (the sign bit cleared, bf16 bits order like their magnitudes).
+__device__ __forceinline__ uint32_t bf16_absmax(uint32_t m, uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, m),
+                                                                __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu)));
+}
+__device__ __forceinline__ uint32_t fold16(uint32_t m) { return max(m & 0xFFFFu, m >> 16); }
+
+// Maximum over aligned groups of W lanes (W a power of two <= 16), every
+// lane of a group ending with it.
+template <int W>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t x) {
+  auto dpp = [](uint32_t v, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, decltype(ctrl)::value, 0xF, 0xF, true);
+  };
+  if constexpr (W >= 2) x = max(x, dpp(x, std::integral_constant<int, 0xB1>{}));
+  if constexpr (W >= 4) x = max(x, dpp(x, std::integral_constant<int, 0x4E>{}));
+  if constexpr (W >= 8) x = max(x, dpp(x, std::integral_constant<int, 0x141>{}));
+  if constexpr (W >= 16) x = max(x, dpp(x, std::integral_constant<int, 0x140>{}));
+  return x;
+}
+
+// Maximum over the whole wave, returned as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = group_max_u32<16>(x);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  x = max(s32[0], s32[1]);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return __builtin_amdgcn_readfirstlane(max(s16[0], s16[1]));
+}
+
+// Binary exponent of a bf16 magnitude (bits without the sign), kNoExp for 0.
+__device__ __forceinline__ int bf16_exp(uint32_t m) { return m ? (int)(m >> 7) - 127 : kNoExp; }
+// Binary exponent of a non-negative fp32 value, kNoExp for 0.
+__device__ __forceinline__ int f32_exp(float x) {
+  return x > 0.f ? (int)((__float_as_uint(x) >> 23) & 0xFFu) - 127 : kNoExp;
+}
+// The state scale exponent for a largest binary exponent M.
+__device__ __forceinline__ int band_exp(int M) { return (M > kNoExp && (M > kBand || M < -kBand)) ? -M : 0; }
+
+// Four bf16 values scaled by 2^a into four fp16 values; ss gets the squares
+// of the scaled values, summed in the order bf16x4_to_f16 uses (a = 0 gives
+// its bits).
+__device__ __forceinline__ u32x2 bf16x4_to_f16_exp(const u32x2& w, int a, float& ss) {
+  const float x0 = __builtin_amdgcn_ldexpf(__uint_as_float(w.x << 16), a);
+  const float x1 = __builtin_amdgcn_ldexpf(__uint_as_float(w.x & 0xFFFF0000u), a);
+  const float x2 = __builtin_amdgcn_ldexpf(__uint_as_float(w.y << 16), a);
+  const float x3 = __builtin_amdgcn_ldexpf(__uint_as_float(w.y & 0xFFFF0000u), a);
+  ss = fmaf(x3, x3, fmaf(x2, x2, fmaf(x1, x1, x0 * x0)));
+  return u32x2{pack_f16(x0, x1), pack_f16(x2, x3)};
+}
+
+// Row factor of a q/k row scaled by 2^a whose scaled squares sum to ss.
+__device__ __forceinline__ float row_factor(bool l2norm, float ss, int a, float eps) {
+  return l2norm ? __builtin_amdgcn_rsqf(ss + __builtin_amdgcn_ldexpf(eps, 2 * a))
+                : __builtin_amdgcn_ldexpf(1.0f, -a);
+}
+
+// ---------------------------------------------------------- chunk walk --
+// A prompt [seq0, seq1) is cut into chunks of up to CT tokens from its first
+// token; a chunk also ends at every checkpoint inside the prompt and the
+// next one starts there.  A run resumed from a checkpoint therefore walks
+// the same chunks as the unbroken run from that point on, and a prompt's
+// chunks do not depend on the rest of the pack.  The walk is uniform over a
+// workgroup; positions come in by scalar loads.
+typedef const int32_t __attribute__((address_space(4)))* ConstI32;
+
+struct ChunkWalk {
+  int pos, end, ci, nck;   // next chunk's first token, prompt end, next checkpoint (index, position)
+  __device__ void init(int seq0, int seq1, int ci0, ConstI32 ck, int n_ck) {
+    pos = seq0;
+    end = seq1;
+    ci = ci0;
+    nck = ci0 < n_ck ? ck[ci0] : INT_MAX;
+  }
+  // The next chunk: its first token in t0, its length returned; ck_at is the
+  // index of the checkpoint it ends on, or -1.
+  __device__ int next(int CT, ConstI32 ck, int n_ck, int& t0, int& ck_at) {
+    t0 = pos;
+    int stop = min(pos + CT, end);
+    ck_at = -1;
+    if (nck <= stop) {
+      stop = nck;
+      ck_at = ci;
+      ++ci;
+      nck = ci < n_ck ? ck[ci] : INT_MAX;
+    }
+    pos = stop;
+    return stop - t0;
+  }
+};
+
+// Number of chunks of the walk above, from the prompt's checkpoints.
+__device__ __forceinline__ int count_chunks(int seq0, int seq1, int ci0, ConstI32 ck, int n_ck, int CT) {
+  int n = 0, p = seq0;
+  for (int i = ci0; i < n_ck; ++i) {
+    const int c = ck[i];
+    if (c >= seq1) break;
+    n += (c - p + CT - 1) / CT;
+    p = c;
+  }
+  return n + (seq1 - p + CT - 1) / CT;
+}
+
 // Two fp32 values as packed bf16 (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
@@ -201,7 +330,8 @@ struct Cfg {
 };
 
 // per-token scalar arrays (index into the scalar block)
-enum { SC_G = 0, SC_BETA, SC_RK, SC_RQ, SC_CK, SC_CQ, SC_CU, SC_LA, SC_LK0, SC_LQ, SC_LK1, SC_PAD };
+// (SC_VM: the chunk's largest |v| as bf16 bits, one word per staging wave)
+enum { SC_G = 0, SC_BETA, SC_RK, SC_RQ, SC_CK, SC_CQ, SC_CU, SC_LA, SC_LK0, SC_LQ, SC_LK1, SC_VM };
 
 template <int DK, int DV>
 __global__ void __launch_bounds__(64 * (DV / 32), 2)
@@ -266,22 +396,27 @@ chunked_prefill_kernel(const ScanArgs a) {
       }
     }
   }
+  // each wave holds 2^E S (E wave-uniform, 0 unless the state or the values
+  // left the band: kBand); stores give S itself, exactly
+  int E = 0;
   auto store_state = [&](float* dst) {
+    auto un = [&](float x) { return E == 0 ? x : __builtin_amdgcn_ldexpf(x, -E); };
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         *reinterpret_cast<float4*>(dst + 32 * kt + 8 * q4 + 4 * g) =
-            make_float4(S[kt][4 * q4], S[kt][4 * q4 + 1], S[kt][4 * q4 + 2], S[kt][4 * q4 + 3]);
+            make_float4(un(S[kt][4 * q4]), un(S[kt][4 * q4 + 1]), un(S[kt][4 * q4 + 2]), un(S[kt][4 * q4 + 3]));
   };
 
-  // checkpoint cursor, uniform over the workgroup; the positions are read
-  // through the constant address space so they come in by scalar loads and
-  // never wait behind the vector loads in flight
-  typedef const int32_t __attribute__((address_space(4)))* ConstI32;
+  // the prompt's chunks (ChunkWalk): cwalk for the chunk being computed,
+  // pwalk one chunk ahead for the prefetch; checkpoint positions come in by
+  // scalar loads, which never wait behind the vector loads in flight
   const ConstI32 ckp = (ConstI32)a.ckpt;
-  int ci = __builtin_amdgcn_readfirstlane(lower_bound_i32(a.ckpt, a.n_ckpt, seq0 + 1));
-  int next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
+  const int ci0 = __builtin_amdgcn_readfirstlane(lower_bound_i32(a.ckpt, a.n_ckpt, seq0 + 1));
+  ChunkWalk cwalk, pwalk;
+  cwalk.init(seq0, seq1, ci0, ckp, a.n_ckpt);
+  pwalk.init(seq0, seq1, ci0, ckp, a.n_ckpt);
 
   // One chunk's HBM rows into registers.  Every lane loads (row index clamped
   // into the chunk, so no load is conditional); rows past the chunk's end are
@@ -328,8 +463,13 @@ chunked_prefill_kernel(const ScanArgs a) {
     for (int u = 0; u < NPV; ++u) ld_v(u, t0x, nx, pv[u]);
     ld_gb(t0x, nx, pg, pb);
   };
+  int pf_t0 = seq0, pf_n = 0;   // the prefetched chunk
   if constexpr (C::PREFETCH)
-    if (seq1 > seq0) fetch(seq0, min(a.chunk, seq1 - seq0));
+    if (seq1 > seq0) {
+      int ck_at;
+      pf_n = pwalk.next(a.chunk, ckp, a.n_ckpt, pf_t0, ck_at);
+      fetch(pf_t0, pf_n);
+    }
   // drain the state and first-chunk loads here, so that no wait inside the
   // chunk loop has to cover them (vmcnt(0); expcnt, lgkmcnt unchanged)
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -347,6 +487,29 @@ chunked_prefill_kernel(const ScanArgs a) {
   // accumulator half serves as the A operand (row v) as well as the B
   // operand (column v)
   auto xqs = [&](f32x16& X, f32x16& QS) {
+    // the scale of this chunk, from the largest |S| entry of the wave's
+    // columns (unscaled: 2^-E times the held value) and the chunk's largest
+    // |v| (recorded at staging, one word per wave)
+    {
+      float ms = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ms = fmaxf(ms, fabsf(S[kt][i]));
+      const int eS = f32_exp(__uint_as_float(wave_max_u32(__float_as_uint(ms))));
+      uint32_t vm = 0;
+#pragma unroll
+      for (int w = 0; w < C::NW; ++w) vm = max(vm, reinterpret_cast<const uint32_t*>(sc)[SC_VM * CT + w]);
+      const int eV = bf16_exp(__builtin_amdgcn_readfirstlane(vm));
+      const int En = band_exp(max(eS == kNoExp ? kNoExp : eS - E, eV));
+      if (En != E) {   // rare: rescale the held state (powers of two, exact)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) S[kt][i] = __builtin_amdgcn_ldexpf(S[kt][i], En - E);
+        E = En;
+      }
+    }
     f16x8 ka[NKS], qa[NKS];
     auto ld = [&](int ks, f16x8& kx, f16x8& qx) {
       const int off = c * LDK + 4 * g + 16 * ks;
@@ -402,8 +565,10 @@ chunked_prefill_kernel(const ScanArgs a) {
   };
 
   int pt0 = 0, pn = 0;   // previous chunk: its O rows are still in the V/O tile
-  for (int t0 = seq0; t0 < seq1; t0 += a.chunk) {
-    const int n = min(a.chunk, seq1 - t0);   // valid rows of this chunk
+  for (;;) {
+    int t0, ck_at;
+    const int n = cwalk.next(a.chunk, ckp, a.n_ckpt, t0, ck_at);   // valid rows of this chunk
+    if (n <= 0) break;
 
     // ---- 1. stage K and Q rows as fp16 (zero past n) with their L2 norms (squares summed in registers, then over
     //         the row's lanes), V rows, betas and the gate cumsum.  The rows
@@ -431,26 +596,54 @@ chunked_prefill_kernel(const ScanArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               if (4 * tg + r >= n) { x.k[r] = z; x.q[r] = z; }
+          // rows converted as they are; a tile whose rows stray from unit
+          // length (rare) is converted again with each such row scaled by
+          // 2^a, its largest element brought into [1, 2) (kQkLo, kQkHi)
+          auto convert = [&](const u32x2 (&xr)[4], uint16_t* dst, const int (&ax)[4], float (&ss)[4]) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 4 * tg + r;
-            x.k[r] = bf16x4_to_f16(x.k[r], sk[r]);
-            x.q[r] = bf16x4_to_f16(x.q[r], sq[r]);
-            *reinterpret_cast<u32x2*>(sK + t * LDK + 4 * kc) = x.k[r];
-            *reinterpret_cast<u32x2*>(sQ + t * LDK + 4 * kc) = x.q[r];
-          }
+            for (int r = 0; r < 4; ++r) {
+              const u32x2 f = bf16x4_to_f16_exp(xr[r], ax[r], ss[r]);
+              *reinterpret_cast<u32x2*>(dst + (4 * tg + r) * LDK + 4 * kc) = f;
+            }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sk[r] = lane_group_total<KC>(sk[r]);
-            sq[r] = lane_group_total<KC>(sq[r]);
-          }
+            for (int r = 0; r < 4; ++r) ss[r] = lane_group_total<KC>(ss[r]);
+          };
+          // whether row r strays (exact in the group's last lane)
+          auto strays = [&](const float (&ss)[4]) {
+            bool any = false;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              any |= kc == KC - 1 && 4 * tg + r < n && !(ss[r] >= kQkLo && ss[r] <= kQkHi);
+            return any;
+          };
+          auto rescale = [&](const u32x2 (&xr)[4], uint16_t* dst, int (&ax)[4], float (&ss)[4]) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              uint32_t m = fold16(bf16_absmax(bf16_absmax(0u, xr[r].x), xr[r].y));
+              m = group_max_u32<KC <= 16 ? KC : 16>(m);
+              if constexpr (KC == 32) {   // the two 16-lane rows of a group
+                const auto sw = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+                m = max(sw[0], sw[1]);
+              }
+              // the row's verdict, from its group's last lane
+              const float tot = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                  4 * ((lane | (KC - 1))), __builtin_bit_cast(int, ss[r])));
+              const bool ok = tot >= kQkLo && tot <= kQkHi;
+              ax[r] = (ok || m == 0 || 4 * tg + r >= n) ? 0 : -bf16_exp(m);
+            }
+            convert(xr, dst, ax, ss);
+          };
+          int ak[4] = {0, 0, 0, 0}, aq[4] = {0, 0, 0, 0};
+          convert(x.k, sK, ak, sk);
+          convert(x.q, sQ, aq, sq);
+          if (__builtin_amdgcn_ballot_w64(strays(sk))) rescale(x.k, sK, ak, sk);
+          if (__builtin_amdgcn_ballot_w64(strays(sq))) rescale(x.q, sQ, aq, sq);
           if (kc == KC - 1) {   // zero-padded rows past n keep r = 1 (no 0 * inf)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int t = 4 * tg + r;
-              const bool nrm = a.l2norm && t < n;
-              sRk[t] = nrm ? __builtin_amdgcn_rsqf(sk[r] + a.eps) : 1.0f;
-              sRq[t] = nrm ? __builtin_amdgcn_rsqf(sq[r] + a.eps) : 1.0f;
+              sRk[t] = t < n ? row_factor(a.l2norm, sk[r], ak[r], a.eps) : 1.0f;
+              sRq[t] = t < n ? row_factor(a.l2norm, sq[r], aq[r], a.eps) : 1.0f;
             }
           }
         }
@@ -459,6 +652,7 @@ chunked_prefill_kernel(const ScanArgs a) {
     {
       // a thread owns the same 16-byte segments of the V/O tile for both
       u32x4 ov[C::NVV];
+      uint32_t vm = 0;   // the chunk's largest |v| (bf16 bits)
 #pragma unroll
       for (int u = 0; u < C::NVV; ++u) {
         const int e = tid + u * NTH;
@@ -470,8 +664,12 @@ chunked_prefill_kernel(const ScanArgs a) {
           ov[u] = *seg;
           if (n < CT && t >= n) vx = u32x4{0u, 0u, 0u, 0u};
           *seg = vx;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vm = bf16_absmax(vm, vx[i]);
         }
       }
+      vm = wave_max_u32(fold16(vm));
+      if (lane == 0) reinterpret_cast<uint32_t*>(sc)[SC_VM * CT + wave] = vm;
       if (wave == 0) {  // betas and the inclusive scan of the log-gates (fixed order),
                         // kept in base 2 so every decay is one v_exp_f32
         const float x = scan32(lane < n ? pg : 0.f) * 1.44269504088896341f;
@@ -490,8 +688,11 @@ chunked_prefill_kernel(const ScanArgs a) {
       }
     }
     __syncthreads();
-    if constexpr (C::PREFETCH)
-      if (t0 + a.chunk < seq1) fetch(t0 + a.chunk, min(a.chunk, seq1 - t0 - a.chunk));
+    if constexpr (C::PREFETCH) {
+      int ck_at2;
+      pf_n = pwalk.next(a.chunk, ckp, a.n_ckpt, pf_t0, ck_at2);
+      if (pf_n > 0) fetch(pf_t0, pf_n);
+    }
 
     f32x16 X, QS;   // K S0^T, Q S0^T for this wave's columns
     // ---- 3. Gram tile -> A (wave 0), K Q^T tile -> P (wave 1), per-token
@@ -643,6 +844,9 @@ chunked_prefill_kernel(const ScanArgs a) {
           vv[4 * q4 + 2] = __uint_as_float(w.y << 16);
           vv[4 * q4 + 3] = __uint_as_float(w.y & 0xFFFF0000u);
         }
+        if (E != 0)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) vv[i] = __builtin_amdgcn_ldexpf(vv[i], E);
       }
       __builtin_amdgcn_sched_barrier(0);
       const f16x8 tA[2] = {lds_op(tr), lds_op(tr + 16)};
@@ -687,6 +891,9 @@ chunked_prefill_kernel(const ScanArgs a) {
       }
       QS = mma(acc_half<0>(U), pA[0], QS);
       QS = mma(acc_half<1>(U), pA[1], QS);
+      if (E != 0)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) QS[i] = __builtin_amdgcn_ldexpf(QS[i], -E);
       // token t's columns 32w + 8 q4 + 4 g .. +3 as 8-byte bf16 pieces into
       // this wave's own columns of the V/O tile (their V was consumed above
       // by this wave only); the rows go to HBM in the next chunk's staging
@@ -712,11 +919,7 @@ chunked_prefill_kernel(const ScanArgs a) {
           S[kt] = mma(kx, uh[h2], S[kt]);
         }
     }
-    if (t0 + n == next_ck) {
-      store_state(a.ckpt_buf + (size_t)ci * sstride + ((size_t)h * DV + v) * DK);
-      ci = __builtin_amdgcn_readfirstlane(ci + 1);
-      next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
-    }
+    if (ck_at >= 0) store_state(a.ckpt_buf + (size_t)ck_at * sstride + ((size_t)h * DV + v) * DK);
     pt0 = t0;
     pn = n;
     __syncthreads();

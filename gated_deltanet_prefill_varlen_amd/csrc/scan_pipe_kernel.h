@@ -22,7 +22,11 @@
 // to even).  Each role runs its own loop with the same barrier count: the
 // state waves keep the state in their registers, the loader waves two
 // chunks' rows in flight in theirs, loaded two intervals ahead of their
-// staging.
+// staging.  Chunks follow ChunkWalk (32 tokens from the prompt's start, cut
+// at every checkpoint); the loader and the state waves each walk them.
+// fp16 range: the loader scales q/k rows far from unit length by a power
+// of two (kQkLo, kQkHi) and records the chunk's largest |v|; each state wave
+// holds its columns as 2^E S (kBand).
 #pragma once
 
 #include "scan_chunked_kernel.h"
@@ -98,8 +102,10 @@ pipelined_prefill_kernel(const ScanArgs a) {
   const int ptid = tid - C::P0;   // loader thread index (negative in the state waves)
   const int j = h / (a.Hv / a.Hqk);
   const int seq0 = a.cu[s], seq1 = a.cu[s + 1];
-  const int nch = (seq1 - seq0 + CT - 1) / CT;
-  auto rows_of = [&](int ch) { return min(CT, seq1 - seq0 - ch * CT); };
+  // checkpoints of this prompt: index of the first, by scalar loads
+  const ConstI32 ckp = (ConstI32)a.ckpt;
+  const int ci0 = __builtin_amdgcn_readfirstlane(lower_bound_i32(a.ckpt, a.n_ckpt, seq0 + 1));
+  const int nch = count_chunks(seq0, seq1, ci0, ckp, a.n_ckpt, CT);
 
   auto slot = [&](int ch) { return smem + (ch & (C::RING - 1)) * C::SLOT; };
   auto ringK = [&](int ch) { return reinterpret_cast<uint16_t*>(slot(ch) + C::rK); };
@@ -137,20 +143,51 @@ pipelined_prefill_kernel(const ScanArgs a) {
         S[kt][4 * q4 + 2] = x.z; S[kt][4 * q4 + 3] = x.w;
       }
   }
+  // the state waves hold 2^E S (E wave-uniform, 0 unless the state or the
+  // values left the band); stores give S itself, exactly
+  int E = 0;
   auto store_state = [&](float* dst) {
+    if (E == 0) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(dst + 32 * kt + 8 * q4 + 4 * g) =
+              make_float4(S[kt][4 * q4], S[kt][4 * q4 + 1], S[kt][4 * q4 + 2], S[kt][4 * q4 + 3]);
+    } else {
+      auto un = [&](float x) { return __builtin_amdgcn_ldexpf(x, -E); };
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(dst + 32 * kt + 8 * q4 + 4 * g) =
+              make_float4(un(S[kt][4 * q4]), un(S[kt][4 * q4 + 1]), un(S[kt][4 * q4 + 2]), un(S[kt][4 * q4 + 3]));
+    }
+  };
+
+  // The scale of the chunk whose scalars are at sc: from the chunk's largest
+  // |v| (recorded by the loader waves) and the largest |S| entry of the
+  // wave's columns (unscaled: 2^-E times the held value); the held state
+  // is rescaled when the scale changes (powers of two, exact).
+  auto choose_scale = [&](const float* sc) {
+    const u32x4 vm4 = *reinterpret_cast<const u32x4*>(sc + SC_VM * CT);
+    __builtin_amdgcn_sched_barrier(0);   // the LDS read first: its latency under the |S| maximum
+    float ms = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<float4*>(dst + 32 * kt + 8 * q4 + 4 * g) =
-            make_float4(S[kt][4 * q4], S[kt][4 * q4 + 1], S[kt][4 * q4 + 2], S[kt][4 * q4 + 3]);
+      for (int i = 0; i < 16; ++i) ms = fmaxf(ms, fabsf(S[kt][i]));
+    const int eS = f32_exp(__uint_as_float(wave_max_u32(__float_as_uint(ms))));
+    const int eV = bf16_exp(__builtin_amdgcn_readfirstlane(max(max(vm4[0], vm4[1]), max(vm4[2], vm4[3]))));
+    const int En = band_exp(max(eS == kNoExp ? kNoExp : eS - E, eV));
+    if (En != E) {   // rare
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kt][i] = __builtin_amdgcn_ldexpf(S[kt][i], En - E);
+      E = En;
+    }
   };
-
-  // checkpoint cursor (state waves), uniform; positions by scalar loads
-  typedef const int32_t __attribute__((address_space(4)))* ConstI32;
-  const ConstI32 ckp = (ConstI32)a.ckpt;
-  int ci = __builtin_amdgcn_readfirstlane(lower_bound_i32(a.ckpt, a.n_ckpt, seq0 + 1));
-  int next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
 
   // ---- a chunk's HBM rows into registers (loader waves), as in
   //      chunked_prefill_kernel: clamped row indices, 32-bit row offsets
@@ -169,9 +206,20 @@ pipelined_prefill_kernel(const ScanArgs a) {
     u32x4 k[2], q[2];   // K and Q row pieces (2 x 8 bf16 each)
     u32x4 v[C::NVV];    // 16-byte V row pieces
     float g, b;         // log-gate and beta of token `lane`
+    int n;              // the chunk's tokens
   };
-  auto fetch = [&](Rows& R, int ch) {
-    const int t0x = seq0 + ch * CT, nx = rows_of(ch);
+  // the loader's walk over the chunks, in fetch order; once past the last
+  // chunk a fetch takes the last chunk's rows again
+  ChunkWalk fwalk;
+  fwalk.init(seq0, seq1, ci0, ckp, a.n_ckpt);
+  int last_t0 = seq0, last_n = 1;
+  auto fetch = [&](Rows& R) {
+    int t0x, ck_at;
+    int nx = fwalk.next(CT, ckp, a.n_ckpt, t0x, ck_at);
+    if (nx <= 0) { t0x = last_t0; nx = last_n; }
+    last_t0 = t0x;
+    last_n = nx;
+    R.n = nx;
     {
       const uint32_t t = min(ptid / 8, nx - 1), pb = 32 * (ptid % 8);
       const uint16_t* kb = kg + (size_t)t0x * a.k_stride + (size_t)j * DK;
@@ -214,34 +262,62 @@ pipelined_prefill_kernel(const ScanArgs a) {
     // -- staging of chunk it into its ring slot
     const int cs = it;
     if (cs < nch) {
-      const int n = rows_of(cs);
+      const int n = R.n;
       uint16_t* sK = ringK(cs);
       uint16_t* sQ = ringQ(cs);
       float* sc = ringSc(cs);
       const int t = ptid / 8, pc = ptid % 8;   // row, 16-dim piece
-      u32x4 kx[2] = {R.k[0], R.k[1]}, qx[2] = {R.q[0], R.q[1]};
+      u32x4 (&kx)[2] = R.k, (&qx)[2] = R.q;   // consumed here, refetched below
       if (t >= n) {   // a prompt's last chunk: rows past n are zeros
         kx[0] = kx[1] = qx[0] = qx[1] = u32x4{0u, 0u, 0u, 0u};
       }
-      float sk = 0.f, sq = 0.f;
+      // rows converted as they are, then, when a row of the wave is far
+      // from unit length (rare), that tile again with each such row scaled
+      // by 2^a (one tile at a time, four values per step, to bound the
+      // registers the rare path holds)
+      auto convert = [&](const u32x4 (&x)[2], uint16_t* dst, int a) {
+        float ss = 0.f;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int w2 = 0; w2 < 2; ++w2) {
-          float s1, s2;
-          const u32x2 kf = bf16x4_to_f16(u32x2{kx[hh][2 * w2], kx[hh][2 * w2 + 1]}, s1);
-          const u32x2 qf = bf16x4_to_f16(u32x2{qx[hh][2 * w2], qx[hh][2 * w2 + 1]}, s2);
-          sk += s1;
-          sq += s2;
-          *reinterpret_cast<u32x2*>(sK + t * LDK + 16 * pc + 8 * hh + 4 * w2) = kf;
-          *reinterpret_cast<u32x2*>(sQ + t * LDK + 16 * pc + 8 * hh + 4 * w2) = qf;
+          for (int w2 = 0; w2 < 2; ++w2) {
+            float s1;
+            const u32x2 f = bf16x4_to_f16_exp(u32x2{x[hh][2 * w2], x[hh][2 * w2 + 1]}, a, s1);
+            ss += s1;
+            *reinterpret_cast<u32x2*>(dst + t * LDK + 16 * pc + 8 * hh + 4 * w2) = f;
+            if (a != 0) __builtin_amdgcn_sched_barrier(0);
+          }
+        return group_sum<8>(ss);
+      };
+      auto rescale = [&](const u32x4 (&x)[2], uint16_t* dst, float& ss) {
+        uint32_t m = 0;   // the row's largest magnitude (bf16 bits)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = bf16_absmax(m, x[hh][i]);
+        m = group_max_u32<8>(fold16(m));
+        const bool ok = ss >= kQkLo && ss <= kQkHi;
+        const int ax = (ok || m == 0 || t >= n) ? 0 : -bf16_exp(m);
+        __builtin_amdgcn_sched_barrier(0);
+        ss = convert(x, dst, ax);
+        return ax;
+      };
+      float sk = convert(kx, sK, 0), sq = convert(qx, sQ, 0);
+      auto off_band = [&](float ss) { return t < n && !(ss >= kQkLo && ss <= kQkHi); };
+      int ak = 0, aq = 0;
+      if (__builtin_amdgcn_ballot_w64(off_band(sk) || off_band(sq))) {   // rare
+        // one copy of the rescaling for both tiles (a run-time pick)
+#pragma unroll 1
+        for (int w = 0; w < 2; ++w) {
+          const u32x4 x[2] = {w ? qx[0] : kx[0], w ? qx[1] : kx[1]};
+          float ss = w ? sq : sk;
+          const int ax = rescale(x, w ? sQ : sK, ss);
+          if (w) { aq = ax; sq = ss; } else { ak = ax; sk = ss; }
         }
-      sk = group_sum<8>(sk);
-      sq = group_sum<8>(sq);
+      }
       if (pc == 7) {   // zero-padded rows keep r = 1
-        const bool nrm = a.l2norm && t < n;
-        sc[SC_RK * CT + t] = nrm ? __builtin_amdgcn_rsqf(sk + a.eps) : 1.0f;
-        sc[SC_RQ * CT + t] = nrm ? __builtin_amdgcn_rsqf(sq + a.eps) : 1.0f;
+        sc[SC_RK * CT + t] = t < n ? row_factor(a.l2norm, sk, ak, a.eps) : 1.0f;
+        sc[SC_RQ * CT + t] = t < n ? row_factor(a.l2norm, sq, aq, a.eps) : 1.0f;
       }
       if (wave == NSW) {   // betas and the base-2 cumsum of the log-gates
         const float xg = scan32(lane < n ? R.g : 0.f) * 1.44269504088896341f;
@@ -252,19 +328,25 @@ pipelined_prefill_kernel(const ScanArgs a) {
       }
     }
     if (cs < nch) {
-      const int n = rows_of(cs);
+      const int n = R.n;
       uint16_t* sV = ringV(cs);
+      uint32_t vm = 0;   // the chunk's largest |v| (bf16 bits), per loader wave
 #pragma unroll
       for (int u = 0; u < C::NVV; ++u) {
         const int e = ptid + u * PTH;
         const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-        *reinterpret_cast<u32x4*>(sV + t * LDV + c8) = t < n ? R.v[u] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 vx = t < n ? R.v[u] : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sV + t * LDV + c8) = vx;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vm = bf16_absmax(vm, vx[i]);
       }
+      vm = wave_max_u32(fold16(vm));
+      if (lane == 0) reinterpret_cast<uint32_t*>(ringSc(cs))[SC_VM * CT + wave - NSW] = vm;
     }
     // -- the rows of chunk it + 2 into R (past the last chunk the last
     //    chunk's rows again: the loads stay unconditional, so the wait for a
     //    set never has to assume the other set was not issued)
-    fetch(R, min(cs + 2, nch - 1));
+    fetch(R);
   };
 
   // the factor waves' part of interval it: Gram and K Q^T tiles of chunk
@@ -386,11 +468,14 @@ pipelined_prefill_kernel(const ScanArgs a) {
   const int nint = (nch + 4) & ~1;
   if (wave < NSW) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the state loads drained before the loop
+    ChunkWalk swalk;
+    swalk.init(seq0, seq1, ci0, ckp, a.n_ckpt);
     for (int it = 0; it < nint; ++it) {
       // ======== state path of chunk it - 3 ========
       const int cx = it - 3;
       if (cx >= 0 && cx < nch) {
-        const int n = rows_of(cx);
+        int t0, ck_at;
+        const int n = swalk.next(CT, ckp, a.n_ckpt, t0, ck_at);
         const uint16_t* sK = ringK(cx);
         const uint16_t* sQ = ringQ(cx);
         uint16_t* sV = ringV(cx);
@@ -399,6 +484,7 @@ pipelined_prefill_kernel(const ScanArgs a) {
         const float* sCk = sc + SC_CK * CT;
         const float* sCq = sc + SC_CQ * CT;
         const float* sCu = sc + SC_CU * CT;
+        if (cx == 0) choose_scale(sc);   // later chunks' scales: at the end of the chunk before
         // X = K S0^T and QS = S0 Q^T for this wave's columns (S0 rounded to
         // fp16 per k tile), then the chunk's decay on S
         f32x16 X = {}, QS = {};
@@ -440,6 +526,9 @@ pipelined_prefill_kernel(const ScanArgs a) {
           vv[4 * q4 + 2] = __uint_as_float(w.y << 16);
           vv[4 * q4 + 3] = __uint_as_float(w.y & 0xFFFF0000u);
         }
+        if (E != 0)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) vv[i] = __builtin_amdgcn_ldexpf(vv[i], E);
         __builtin_amdgcn_sched_barrier(0);
         const f16x8 tA[2] = {lds_op(tr), lds_op(tr + 16)};
         // Y = beta (V - r_k e^G X), in place of X (rows past n: exact zeros)
@@ -489,19 +578,20 @@ pipelined_prefill_kernel(const ScanArgs a) {
         // wave's 32 columns of row t go to HBM as four 8-byte bf16 pieces
         QS = mma(uo[0], pA[0], QS);
         QS = mma(uo[1], pA[1], QS);
+        if (E != 0)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) QS[i] = __builtin_amdgcn_ldexpf(QS[i], -E);
         if (c < n) {
-          uint16_t* orow = og + (size_t)(seq0 + cx * CT + c) * a.Hv * DV + 32 * wave + 4 * g;
+          uint16_t* orow = og + (size_t)(t0 + c) * a.Hv * DV + 32 * wave + 4 * g;
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4)
             *reinterpret_cast<u32x2*>(orow + 8 * q4) =
                 u32x2{pack_bf16(QS[4 * q4], QS[4 * q4 + 1]), pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3])};
         }
-        const int t_end = seq0 + cx * CT + n;
-        if (t_end == next_ck) {
-          store_state(a.ckpt_buf + (size_t)ci * sstride + ((size_t)h * DV + v) * DK);
-          ci = __builtin_amdgcn_readfirstlane(ci + 1);
-          next_ck = ci < a.n_ckpt ? ckp[ci] : INT_MAX;
-        }
+        if (ck_at >= 0) store_state(a.ckpt_buf + (size_t)ck_at * sstride + ((size_t)h * DV + v) * DK);
+        // the next chunk's scale, here where the state waves would otherwise
+        // wait at the barrier (that chunk's scalars were staged two intervals ago)
+        if (cx + 1 < nch) choose_scale(ringSc(cx + 1));
       }
       __syncthreads();
     }
@@ -512,9 +602,9 @@ pipelined_prefill_kernel(const ScanArgs a) {
     }
   } else if (nch > 0) {
     Rows R0, R1;
-    fetch(R0, 0);
+    fetch(R0);
     __builtin_amdgcn_sched_barrier(0);   // chunk 0's loads first: the first staging waits for them alone
-    fetch(R1, min(1, nch - 1));
+    fetch(R1);
     for (int it = 0; it < nint; it += 2) {   // two intervals per trip: R0 even, R1 odd
       load_stage(R0, it);
       __syncthreads();

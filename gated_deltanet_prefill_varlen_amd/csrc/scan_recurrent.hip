@@ -149,21 +149,72 @@ decode_kernel(const DecodeArgs a) {
   const int rg = blockIdx.z * kRows * RPT + tid / LPR;
   const int jl = tid % LPR;
   const int j = h / (a.Hv / a.Hqk);
-  // a token's inputs do not depend on the slot: token 0's are requested
-  // before the slot -> state address round trip
+  // a token's inputs do not depend on the slot: without the conv, token 0's
+  // are requested before the slot -> state address round trip
   float kv[16], qv[16], vrow[RPT], galpha, gbeta;
+  const bool conv = a.conv_w != nullptr;
+  int r = 0;
+  // With the conv, q, k and v are its inputs: the value of channel c at token
+  // n is conv4_silu over the channel's inputs at n-3 .. n (before the
+  // sequence's first token, its slot's conv state), rounded to the io dtype
+  // as a stored conv output would be (channels ordered q | k | v).
+  const T* cst = static_cast<const T*>(a.conv_state);
+  auto conv_in4 = [&](const T* x, int64_t stride, int p, int ch, float* out) {
+    if (p >= 0) load4<IO>(x + ((size_t)b * a.n_tok + p) * stride, out);
+    else load4<IO>(cst + ((size_t)r * 3 + 3 + p) * a.conv_dim + ch, out);
+  };
+  auto conv_row16 = [&](const T* x, int64_t stride, int ch0, int n, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 4 * LPR * i + 4 * jl;
+      float xw[4][4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) conv_in4(x + d0, stride, n - 3 + p, ch0 + d0, xw[p]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float4 w = reinterpret_cast<const float4*>(a.conv_w)[ch0 + d0 + e];
+        const float y = conv4_silu(w.x, w.y, w.z, w.w, xw[0][e], xw[1][e], xw[2][e], xw[3][e]);
+        out[4 * i + e] = IO::kBytes == 2 ? round_bf16(y) : y;
+      }
+    }
+  };
   auto load_tok = [&](int n) {
     const size_t t = (size_t)b * a.n_tok + n;
-    load_row16<LPR, IO>(static_cast<const T*>(a.k) + t * a.k_stride + j * DK, jl, kv);
-    load_row16<LPR, IO>(static_cast<const T*>(a.q) + t * a.q_stride + j * DK, jl, qv);
+    if (conv) {
+      const int nq = a.Hqk * DK;
+      conv_row16(static_cast<const T*>(a.k) + j * DK, a.k_stride, nq + j * DK, n, kv);
+      conv_row16(static_cast<const T*>(a.q) + j * DK, a.q_stride, j * DK, n, qv);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      vrow[i] = load1<IO>(static_cast<const T*>(a.v) + t * a.v_stride + (size_t)h * DV + rg + kRows * i);
+      for (int i = 0; i < RPT; ++i) {
+        const int col = h * DV + rg + kRows * i, ch = 2 * nq + col;
+        float xw[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int pp = n - 3 + p;
+          xw[p] = pp >= 0 ? load1<IO>(static_cast<const T*>(a.v) + ((size_t)b * a.n_tok + pp) * a.v_stride + col)
+                          : load1<IO>(cst + ((size_t)r * 3 + 3 + pp) * a.conv_dim + ch);
+        }
+        const float4 w = reinterpret_cast<const float4*>(a.conv_w)[ch];
+        const float y = conv4_silu(w.x, w.y, w.z, w.w, xw[0], xw[1], xw[2], xw[3]);
+        vrow[i] = IO::kBytes == 2 ? round_bf16(y) : y;
+      }
+    } else {
+      load_row16<LPR, IO>(static_cast<const T*>(a.k) + t * a.k_stride + j * DK, jl, kv);
+      load_row16<LPR, IO>(static_cast<const T*>(a.q) + t * a.q_stride + j * DK, jl, qv);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        vrow[i] = load1<IO>(static_cast<const T*>(a.v) + t * a.v_stride + (size_t)h * DV + rg + kRows * i);
+    }
     galpha = a.g[t * a.Hv + h];
     gbeta = a.beta[t * a.Hv + h];
   };
-  load_tok(0);
-  const int r = a.slot ? a.slot[b] : b;
+  if (conv) {
+    r = a.slot ? a.slot[b] : b;
+    load_tok(0);
+  } else {
+    load_tok(0);
+    r = a.slot ? a.slot[b] : b;
+  }
   float* sp = a.state + ((size_t)r * a.Hv + h) * DV * DK;
   float S[RPT][16];
 #pragma unroll
@@ -187,6 +238,36 @@ decode_kernel(const DecodeArgs a) {
   for (int i = 0; i < RPT; ++i) store_row16f<LPR>(sp + (size_t)(rg + kRows * i) * DK, jl, S[i]);
 }
 
+// The conv state of each decoding sequence's slot moves on by n_tok inputs:
+// entry j becomes the input at position n_tok - 3 + j (from the tokens' own
+// inputs, or the old state when n_tok < 3).  A launch of its own after the
+// decode, which reads the old states.  Four channels per thread; every read
+// comes before every write of the same thread's channels.
+template <typename IO>
+__global__ void __launch_bounds__(256) conv_shift_kernel(const DecodeArgs a) {
+  using T = typename IO::T;
+  const int b = blockIdx.x;
+  const int c0 = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c0 >= a.conv_dim) return;
+  const int r = a.slot ? a.slot[b] : b;
+  T* cst = static_cast<T*>(a.conv_state) + (size_t)r * 3 * a.conv_dim + c0;
+  const int nq = a.Hqk * a.dk;
+  const T* x;
+  int64_t stride;
+  if (c0 < nq) { x = static_cast<const T*>(a.q) + c0; stride = a.q_stride; }
+  else if (c0 < 2 * nq) { x = static_cast<const T*>(a.k) + (c0 - nq); stride = a.k_stride; }
+  else { x = static_cast<const T*>(a.v) + (c0 - 2 * nq); stride = a.v_stride; }
+  float v[3][4];
+#pragma unroll
+  for (int jj = 0; jj < 3; ++jj) {
+    const int p = a.n_tok - 3 + jj;
+    if (p >= 0) load4<IO>(x + ((size_t)b * a.n_tok + p) * stride, v[jj]);
+    else load4<IO>(cst + (size_t)(3 + p) * a.conv_dim, v[jj]);
+  }
+#pragma unroll
+  for (int jj = 0; jj < 3; ++jj) store4<IO>(cst + (size_t)jj * a.conv_dim, v[jj]);
+}
+
 template <int DK, int DV, typename IO>
 hipError_t launch_rec_prefill(const ScanArgs& a, hipStream_t st) {
   dim3 grid(a.n_seqs, a.Hv, DV / kRows);
@@ -208,6 +289,12 @@ hipError_t launch_dec(const DecodeArgs& a, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((decode_kernel<DK, DV, RPT, IO>), dim3(a.batch, a.Hv, DV / (kRows * RPT)),
                        dim3(kRows * (DK / 16)), 0, st, a);
+  }
+  if (a.conv_w) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((conv_shift_kernel<IO>), dim3(a.batch, (a.conv_dim + 1023) / 1024), dim3(256), 0, st,
+                       a);
   }
   return hipGetLastError();
 }

@@ -29,8 +29,10 @@
  *   - Work is asynchronous on the given stream (a hipStream_t passed as
  *     void*; NULL = the null stream).  The library keeps no global mutable
  *     state and shares no scratch memory between calls or streams.
- *   - Launch configuration depends only on the shape struct, never on the
- *     number of prompts, their lengths or their order.
+ *   - Each (prompt, head)'s arithmetic depends only on that prompt's own
+ *     inputs, initial state and checkpoint positions: never on the grid, the
+ *     other prompts of the pack or their order (the launch grid itself does
+ *     depend on the number of prompts).
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -54,7 +56,7 @@ typedef enum gdn_status {
   GDN_ERR_SHAPE = 2,       /* negative count, bad stride or inconsistent sizes            */
   GDN_ERR_UNSUPPORTED = 3, /* head dims, chunk, dtype, flags or head ratio not built      */
   GDN_ERR_SEQLENS = 4,     /* cu_seqlens not 0-based, non-decreasing, ending at n_tokens  */
-  GDN_ERR_CKPT = 5,        /* checkpoints unsorted, outside a prompt or off its chunk grid */
+  GDN_ERR_CKPT = 5,        /* checkpoints not strictly increasing, or outside every prompt */
   GDN_ERR_CAPACITY = 6,    /* an output list is too short, or a slot outside the pool      */
   GDN_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed                  */
 } gdn_status;
@@ -67,8 +69,12 @@ typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
 /* Layer geometry and numeric options, passed by pointer to every call.
  *   num_qk_heads, num_v_heads: Hqk and Hv, Hv a multiple of Hqk.
  *   head_k_dim, head_v_dim:    dk and dv, each one of 32, 64, 128.
- *   chunk:                     tokens per chunk of the chunked scan, one of 16,
- *                              32, 64; checkpoints must sit on this grid.
+ *   chunk:                     the most tokens one chunk of the chunked scan
+ *                              holds, one of 16, 32, 64.  The scans run chunks
+ *                              of min(chunk, 32) tokens from each prompt's first
+ *                              token (a 64-token chunk's end state is the same
+ *                              quantity as two 32-token chunks'), and a chunk
+ *                              also ends at every checkpoint.
  *   io_dtype:                  gdn_dtype of q, k, v, out, x, y, conv states.
  *   flags:                     GDN_QK_L2NORM or 0.
  *   scale:                     factor on the outputs (1.0 for none).
@@ -159,18 +165,29 @@ GDN_API gdn_status gdn_conv1d_silu_packed(const gdn_shape* shape, const int32_t*
  *   ckpt_positions:   device int32 [n_ckpt] global pack offsets, strictly
  *                     increasing; ckpt_positions_host its host mirror.  A
  *                     position p belongs to the prompt with cu[s] < p <=
- *                     cu[s+1] and must satisfy (p - cu[s]) % chunk == 0; the
- *                     checkpoint is the state after the prompt's first
- *                     p - cu[s] tokens.  gdn_plan_checkpoints makes such lists.
+ *                     cu[s+1]; the checkpoint is the state after the
+ *                     prompt's first p - cu[s] tokens.  Any such position
+ *                     works: the scan ends a chunk there and starts the
+ *                     next one at p, so a prompt resumed from a checkpoint
+ *                     (init_state = that checkpoint, the prompt's later
+ *                     tokens, the later checkpoints) gives the unbroken run's
+ *                     outputs, checkpoints and final state bit for bit.
+ *                     gdn_plan_checkpoints makes such lists, also for
+ *                     prompts resumed at an absolute position p0.
  *   out:              device io_dtype [n_tokens, Hv, dv] (dense).
  *   final_state:      device fp32 [n_seqs, Hv, dv, dk] or NULL (not written).
  *   ckpt_buf:         device fp32 [n_ckpt, Hv, dv, dk]; may be NULL iff n_ckpt = 0.
  * Arithmetic: states are carried and accumulated in fp32.  With bf16 io the
- * scan's products run on fp16 matrix-core operands: the raw q/k rows convert
- * to fp16 exactly, the fp32 values entering a product (state, T, P, Y, U) are
- * rounded to fp16 once, which holds states to about 4e-4 relative Frobenius
- * against exact arithmetic while q/k elements, the state's entries and the
- * update values stay inside fp16's normal range (about 6e-5 .. 65504); with
+ * scan's products run on fp16 matrix-core operands: q/k rows convert to fp16
+ * exactly while their sum of squares lies in [2^-4, 2^20], other rows are
+ * scaled by a power of two first (the factor folded into the row's norm);
+ * the state is held per 32 state columns as 2^E S, E chosen per chunk from
+ * the largest |S| entry and the chunk's largest |v| (0 while both lie in
+ * [2^-6, 2^7)); the fp32 values entering a product (state, T, P, Y, U) are
+ * rounded to fp16 once.  This holds states to about 4e-4 relative Frobenius
+ * against exact arithmetic at any input scale inside fp32's range, as long
+ * as the |v| rows of one 32-token chunk lie within about 2^14 of each other
+ * (rows far below the chunk's largest reach fp16's subnormal range).  With
  * fp32 io a token-recurrent fp32 kernel runs instead.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS,
  * GDN_ERR_CKPT, GDN_ERR_HIP.  init_state may alias final_state. */
@@ -184,7 +201,8 @@ GDN_API gdn_status gdn_prefill_packed(const gdn_shape* shape, const int32_t* cu_
 
 /* One recurrent step for each of `batch` decoding sequences, in place on a
  * state pool (one forward pass carries decodes beside a packed prefill:
- * sparkinfer release v0.6.4, "What changed").
+ * sparkinfer release v0.6.4, "What changed"; packed GDN decode: vllm.cpp
+ * docs, "vLLM, online serving", lever 2b).
  *   q, k:       device io_dtype [batch, Hqk, dk] (token stride from shape);
  *   v:          [batch, Hv, dv];  g, beta: device fp32 [batch, Hv].
  *   state:      device fp32 [pool_slots, Hv, dv, dk], updated in place.
@@ -192,20 +210,31 @@ GDN_API gdn_status gdn_prefill_packed(const gdn_shape* shape, const int32_t* cu_
  *               slot_host its host mirror (required with slot): every entry
  *               in [0, pool_slots) and all distinct.
  *   out:        device io_dtype [batch, Hv, dv].
+ *   conv_w:     device fp32 [conv_dim, 4] or NULL; conv_state: device io_dtype
+ *               [pool_slots, 3, conv_dim] or NULL (both or neither;
+ *               conv_dim = 2*Hqk*dk + Hv*dv, channels [q | k | v]).  With
+ *               them, q, k and v are the inputs of the short convolution
+ *               (gdn_conv1d_silu_packed's x): each channel's value is the
+ *               width-4 conv + SiLU over its last three inputs (the slot's
+ *               conv_state, oldest first) and the current one, rounded to
+ *               io_dtype as a stored conv output is, in the same operation
+ *               order, so the results equal gdn_conv1d_silu_packed followed
+ *               by this call without the conv, bit for bit.  The slot's
+ *               conv_state then holds its last three inputs.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_CAPACITY
  * (slot outside the pool, repeated, or batch > pool_slots without slots),
  * GDN_ERR_HIP. */
 GDN_API gdn_status gdn_decode_step(const gdn_shape* shape, int32_t batch, const void* q, const void* k,
                            const void* v, const float* g, const float* beta, float* state,
                            int64_t pool_slots, const int32_t* slot, const int32_t* slot_host,
-                           void* out, void* stream);
+                           void* out, const float* conv_w, void* conv_state, void* stream);
 
 /* n_tok recurrent steps for each of `batch` decoding sequences, in place on
  * the state pool, keeping the state after every token: the verification pass
  * of speculative or multi-token-prediction decoding, where a rejected suffix
- * is rolled back by restoring a kept state (sparkinfer README, supported
- * speculation: draft-model and multi-token prediction; Qwen3-Next uses
- * multi-token prediction).  gdn_decode_step is the n_tok = 1 case.
+ * is rolled back by restoring a kept state (vllm-ascend tutorial,
+ * Qwen3.6-35B-A3B, section 9.3 "Model-Specific Optimizations": MTP
+ * speculative decoding).  gdn_decode_step is the n_tok = 1 case.
  *   n_tok:      tokens per sequence, >= 1.
  *   q, k:       device io_dtype [batch * n_tok, Hqk, dk], sequence-major (row
  *               b * n_tok + i is token i of sequence b; token stride from
@@ -217,12 +246,17 @@ GDN_API gdn_status gdn_decode_step(const gdn_shape* shape, int32_t batch, const 
  *   out:        device io_dtype [batch * n_tok, Hv, dv].
  *   snapshots:  device fp32 [batch, n_tok, Hv, dv, dk] (entry i: the state
  *               after token i of the sequence), or NULL.
+ *   conv_w, conv_state: as in gdn_decode_step; token i's window reaches back
+ *               into the sequence's earlier tokens of this call, then into
+ *               the slot's conv state, which ends at the last three inputs.
+ *               (A rollback restores it from the call's own inputs.)
  * The arithmetic per token is gdn_decode_step's, so n_tok calls of it give
  * the same bits.  Errors: as gdn_decode_step (n_tok < 1: GDN_ERR_SHAPE). */
 GDN_API gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t batch, int32_t n_tok, const void* q,
                              const void* k, const void* v, const float* g, const float* beta,
                              float* state, int64_t pool_slots, const int32_t* slot,
-                             const int32_t* slot_host, void* out, float* snapshots, void* stream);
+                             const int32_t* slot_host, void* out, float* snapshots,
+                             const float* conv_w, void* conv_state, void* stream);
 
 /* Checkpoint copy on its own stream (sparkinfer release v0.6.28: the scan and
  * the checkpoint copy of checkpointing prompts run on their own streams, and

@@ -55,6 +55,29 @@ def test_planner_matches_oracle_planner():
                 np.testing.assert_array_equal(got, want)
 
 
+@no_gpu
+def test_planner_output_passes_validation_with_p0_off_the_chunk_grid():
+    """A prompt continued from an absolute position p0 that is not a
+    multiple of the chunk (a prompt cut by the pass's token budget and
+    resumed in the next pass) gets checkpoints off its chunk grid; the
+    planner's list is accepted as it is."""
+    cu = np.array([0, 300], np.int32)
+    ck = gdn.gdn_plan_checkpoints(cu, 256, 16, np.array([137], np.int32))
+    np.testing.assert_array_equal(ck, [119])
+    assert 119 % 16 != 0
+    sh = gdn.make_shape(2, 2, 32, 32, 16, gdn.GDN_F32)
+    assert _prefill_call(sh, cu=tuple(cu), ck=tuple(ck)) == 7   # validated; no device to launch on
+    rng = np.random.default_rng(5)
+    for trial in range(50):
+        lens = rng.integers(0, 700, size=int(rng.integers(1, 6)))
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        p0 = rng.integers(0, 2000, size=len(lens)).astype(np.int32)
+        ck = gdn.gdn_plan_checkpoints(cu, 256, 16, p0)
+        np.testing.assert_array_equal(ck, O.plan_checkpoints(cu, 256, 16, p0=p0))
+        if len(ck):
+            assert _prefill_call(sh, cu=tuple(cu), ck=tuple(ck)) == 7
+
+
 def test_planner_errors_and_capacity():
     lib = gdn.load()
     cu = np.array([0, 1024, 2048], np.int32)
@@ -102,7 +125,10 @@ def test_prefill_validation_errors():
     assert _prefill_call(cu=(0, 40, 64), T=65) == 4
     assert _prefill_call(q=0) == 1
     assert _prefill_call(ck=(32, 16)) == 5          # not increasing
-    assert _prefill_call(ck=(8,)) == 5              # off the 16-token chunk grid
+    # any position inside a prompt passes validation (the scan ends a chunk
+    # there); without a GPU the call then fails at its launch (GDN_ERR_HIP)
+    assert _prefill_call(ck=(8,)) == 7
+    assert _prefill_call(ck=(40, 41)) == 7
     assert _prefill_call(ck=(0,)) == 5              # not inside a prompt
     assert _prefill_call(ck=(80,)) == 5             # past the pack
     assert _prefill_call(ck=(16,), ckbuf=False) == 1
@@ -120,20 +146,25 @@ def test_empty_pack_is_ok_without_any_launch():
 def test_decode_validation_errors():
     lib = gdn.load()
     sh = gdn.make_shape(2, 4, 32, 32, 16)
-    def call(batch=3, pool=5, slot=None):
+    def call(batch=3, pool=5, slot=None, cw=None, cs=None):
         sl = None if slot is None else np.asarray(slot, np.int32)
         return lib.gdn_decode_step(ctypes.byref(sh), batch, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, pool,
                                    FAKE if sl is not None else None,
-                                   sl.ctypes.data if sl is not None else None, FAKE, None)
+                                   sl.ctypes.data if sl is not None else None, FAKE, cw, cs, None)
     assert call(batch=0) == 0
     assert call(batch=6, pool=5) == 6
     assert call(slot=[0, 1, 1]) == 6
     assert call(slot=[0, 1, 5]) == 6
     assert call(slot=[0, -1, 2]) == 6
+    assert call(cw=FAKE) == 1                       # conv weights without conv states
+    assert call(cs=FAKE) == 1                       # and the other way round
+    assert call(cw=FAKE, cs=FAKE + 4) == 2          # misaligned conv state
     assert lib.gdn_decode_step(ctypes.byref(sh), 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, FAKE, None,
-                               FAKE, None) == 1
+                               FAKE, None, None, None) == 1
     assert lib.gdn_decode_step(ctypes.byref(sh), 3, None, FAKE, FAKE, FAKE, FAKE, FAKE, 5, None, None,
-                               FAKE, None) == 1
+                               FAKE, None, None, None) == 1
+    assert lib.gdn_decode_tokens(ctypes.byref(sh), 3, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, None,
+                                 None, FAKE, None, None, None, None) == 2
 
 
 @no_gpu

@@ -96,6 +96,71 @@ def _unit(x):
     return (x / np.linalg.norm(x, axis=-1, keepdims=True)).astype(np.float32)
 
 
+@pytest.mark.parametrize("n,d,dtype", [(1, 128, "bf16"), (4, 128, "bf16"), (2, 64, "bf16"), (3, 32, "f32")])
+def test_decode_with_conv_window_shift(n, d, dtype):
+    """Decode with the short convolution applied per token: q, k, v are the
+    conv's inputs, each slot's conv window supplies the history and moves on
+    by the call's tokens.  Against the oracle's conv (history = the slot's
+    window, output rounded to the io dtype) followed by its decode, with a
+    permuted slot pool; and bitwise against gdn_conv1d_silu_packed followed by
+    gdn_decode_tokens without the conv (same operation order)."""
+    B, Hqk, Hv, P = 6, 2, 4, 11
+    rng = np.random.default_rng(100 + n + d)
+    C = 2 * Hqk * d + Hv * d
+    enc = (lambda a: W.f32_to_bf16_bits(a.astype(np.float32))) if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    x = enc(rng.standard_normal((B * n, C)))                   # pre-conv rows, channels q | k | v
+    w = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    cstate = enc(rng.standard_normal((P, 3, C)))
+    g = (-np.log1p(np.exp(rng.standard_normal((B * n, Hv))))).astype(np.float32)
+    beta = (1 / (1 + np.exp(-rng.standard_normal((B * n, Hv))))).astype(np.float32)
+    state = (0.1 * rng.standard_normal((P, Hv, d, d))).astype(np.float32)
+    slot = rng.permutation(P)[:B].astype(np.int32)
+    nq = Hqk * d
+    io = gdn.GDN_BF16 if dtype == "bf16" else gdn.GDN_F32
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xt = io_tensor(x, dtype)
+    shape = gdn.make_shape(Hqk, Hv, d, d, 64, io, q_tok_stride=C, k_tok_stride=C, v_tok_stride=C)
+    st, cs = f32_tensor(state), io_tensor(cstate, dtype)
+    out = torch.empty((B * n, Hv, d), dtype=tdt, device=DEV)
+    snaps = torch.empty((B, n, Hv, d, d), dtype=torch.float32, device=DEV)
+    wt = f32_tensor(w)
+    gdn.gdn_decode_tokens(shape, n, xt[:, :nq], xt[:, nq:2 * nq], xt[:, 2 * nq:], f32_tensor(g),
+                          f32_tensor(beta), st, i32_tensor(slot), slot, out, snaps, conv_w=wt, conv_state=cs)
+    torch.cuda.synchronize()
+
+    # oracle: conv per sequence from its slot's window, rounded as stored, then decode
+    xf = O.to_f64(x, dtype)
+    cu = np.arange(B + 1) * n
+    y, cs_out, _ = O.conv1d_silu_packed(xf, w.astype(np.float64), cu, O.to_f64(cstate, dtype)[slot])
+    if dtype == "bf16":
+        y = O.round_bf16(y)
+    qf = y[:, :nq].reshape(B * n, Hqk, d)
+    kf = y[:, nq:2 * nq].reshape(B * n, Hqk, d)
+    vf = y[:, 2 * nq:].reshape(B * n, Hv, d)
+    ro, rs, rsn = O.decode_tokens(qf, kf, vf, g.astype(np.float64), beta.astype(np.float64),
+                                  state.astype(np.float64), n, slot)
+    assert np.max(O.max_rel_rows(to_f64(out), ro)) <= OUT_TOL[dtype]
+    assert np.max(O.rel_frobenius(to_f64(st)[slot], rs[slot])) <= STATE_TOL
+    assert np.max(O.rel_frobenius(to_f64(snaps).reshape(B * n, Hv, d, d), rsn.reshape(B * n, Hv, d, d))) <= STATE_TOL
+    got_cs = to_f64(cs)
+    np.testing.assert_array_equal(got_cs[slot], cs_out)          # the windows moved on exactly
+    untouched = np.setdiff1d(np.arange(P), slot)
+    np.testing.assert_array_equal(got_cs[untouched], O.to_f64(cstate, dtype)[untouched])
+    np.testing.assert_array_equal(to_f64(st)[untouched], state[untouched].astype(np.float64))
+
+    # the two-call path: the packed conv, then the decode on its outputs
+    yt = torch.empty_like(xt)
+    cs_in = io_tensor(cstate, dtype)[torch.from_numpy(slot).long().to(DEV)].contiguous()
+    gdn.gdn_conv1d_silu_packed(shape, i32_tensor(cu), cu, xt, wt, yt, conv_state_in=cs_in)
+    st2 = f32_tensor(state)
+    out2 = torch.empty_like(out)
+    snaps2 = torch.empty_like(snaps)
+    gdn.gdn_decode_tokens(shape, n, yt[:, :nq], yt[:, nq:2 * nq], yt[:, 2 * nq:], f32_tensor(g),
+                          f32_tensor(beta), st2, i32_tensor(slot), slot, out2, snaps2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(st, st2) and torch.equal(snaps, snaps2)
+
+
 def test_decode_identity_slots_and_small_heads():
     d = W.decode_batch(seed=4, batch=5, Hqk=2, Hv=4, dk=32, dv=64)
     q, k, v, g, b, st, _, out = _decode_dev(d)
