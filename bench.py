@@ -48,10 +48,26 @@ def prefill_alg_bytes(p, n_ckpt: int, init_nonzero: bool) -> int:
     return p.n_tokens * per_tok + p.n_seqs * state * (2 if init_nonzero else 1) + n_ckpt * state
 
 
+def kernel_chunk(p) -> int:
+    """Tokens per chunk the scan runs: min(chunk, 32) (a 64-token chunk's end
+    state is the same quantity as two 32-token chunks')."""
+    return min(p.chunk, 32)
+
+
 def prefill_alg_flops(p) -> float:
-    """Chunked form, per token per value head: 2C(3dk + 2dv) + 6 dk dv + C^2/3."""
-    C, dk, dv = p.chunk, p.dk, p.dv
+    """Chunked form at the executed chunk C, per token per value head:
+    2C(3dk + 2dv) + 6 dk dv + C^2/3."""
+    C, dk, dv = kernel_chunk(p), p.dk, p.dv
     return p.n_tokens * p.Hv * (2 * C * (3 * dk + 2 * dv) + 6 * dk * dv + C * C / 3)
+
+
+def step_min_bytes(p, n_ckpt: int) -> int:
+    """The fewest bytes one pass of the whole step can move (conv fused into
+    the scan, checkpoints written once into the pool): the pre-conv rows x in
+    (as many bytes as q, k, v), g and beta in, out, the final states and each
+    checkpoint once, the conv weights and each prompt's conv state."""
+    C = 2 * p.Hqk * p.dk + p.Hv * p.dv
+    return prefill_alg_bytes(p, n_ckpt, p.init is not None) + C * 4 * 4 + p.n_seqs * 3 * C * 2
 
 
 def csrc_digest() -> str:
@@ -164,7 +180,9 @@ def bench_prefill(torch, gdn, p, steps, warmup, stream, flush, label):
         for _ in range(warmup):
             dp.run(stream=stream)
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
         times = Timer(torch, stream).run(lambda: dp.run(stream=stream), steps, flush)
+        wall_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
     med = statistics.median(times)
     B = prefill_alg_bytes(p, len(ck), p.init is not None)
@@ -176,6 +194,7 @@ def bench_prefill(torch, gdn, p, steps, warmup, stream, flush, label):
         "ms_p10": float(np.percentile(times, 10)), "ms_p90": float(np.percentile(times, 90)),
         "tokens_per_s": p.n_tokens / (med * 1e-3), "alg_bytes": B, "alg_flops": F,
         "achieved_GBs": B / (med * 1e-3) / 1e9, "roofline_frac": t_roof / (med * 1e-3),
+        "wall_ms_timed": wall_ms,
     }
     del dp
     return res, times
@@ -296,6 +315,7 @@ def bench_layer_step(torch, gdn, p, steps, warmup, stream, label):
                              "scan_ms_median": statistics.median(scan_b_ms)},
         "scan_alg_bytes": B_scan, "scan_alg_flops": F,
         "step_alg_bytes": B_scan + B_conv + B_copy,
+        "step_min_bytes": step_min_bytes(p, n_ck),
         "copy_exact": exact,
     }
 
@@ -396,6 +416,32 @@ def bench_decode(torch, gdn, stream, flush, reps):
     med = statistics.median(times)
     B = 32 * 32 * 128 * 128 * 4 * 2 + 32 * (2 * 16 * 128 * 2 + 32 * 128 * 2 * 2 + 32 * 8)
     return {"workload": "decode 32 seqs x 32 heads, fp32 state in place", "ms_median": med,
+            "achieved_GBs": B / (med * 1e-3) / 1e9, "roofline_frac": B / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_decode_conv(torch, gdn, stream, flush, reps):
+    """The decode batch with the short conv applied in the decode kernel:
+    q, k, v are the conv's inputs, each slot's conv window supplies the
+    history and is moved on by a second launch."""
+    import workloads as W
+    d = W.decode_batch(seed=0, batch=32, pool=64)
+    C = 2 * 16 * 128 + 32 * 128
+    rng = np.random.default_rng(1)
+    x = torch.from_numpy(W.f32_to_bf16_bits(rng.standard_normal((32, C)).astype(np.float32))).view(torch.bfloat16).to("cuda:0")
+    w = f32_t(torch, (0.5 * rng.standard_normal((C, 4))).astype(np.float32))
+    cs = torch.from_numpy(W.f32_to_bf16_bits(rng.standard_normal((64, 3, C)).astype(np.float32))).view(torch.bfloat16).to("cuda:0")
+    g, b = f32_t(torch, d.g), f32_t(torch, d.beta)
+    st, slot = f32_t(torch, d.state), i32_t(torch, d.slot)
+    out = torch.empty((32, 32, 128), dtype=torch.bfloat16, device="cuda:0")
+    shape = gdn.make_shape(16, 32, 128, 128, 64, q_tok_stride=C, k_tok_stride=C, v_tok_stride=C)
+    nq = 16 * 128
+    fn = lambda: gdn.gdn_decode_step(shape, x[:, :nq], x[:, nq:2 * nq], x[:, 2 * nq:], g, b, st, slot, d.slot,
+                                     out, conv_w=w, conv_state=cs, stream=stream)
+    fn()
+    times = Timer(torch, stream).run(fn, reps, flush)
+    med = statistics.median(times)
+    B = 32 * 32 * 128 * 128 * 4 * 2 + 32 * (C * 2 + 2 * 3 * C * 2 + 32 * 128 * 2 + 32 * 8) + C * 16
+    return {"workload": "decode 32 seqs x 32 heads with the conv (windows in a slot pool)", "ms_median": med,
             "achieved_GBs": B / (med * 1e-3) / 1e9, "roofline_frac": B / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
@@ -554,6 +600,8 @@ def cpu_baseline(p, n_prompts: int):
     t0 = time.perf_counter()
     with ctx.Pool(procs) as pool:
         per = pool.map(_oracle_one_prompt, jobs)
+        pool.close()   # workers leave by themselves (the context's exit would signal them)
+        pool.join()
     wall = time.perf_counter() - t0
     toks = sum(j[0].shape[0] for j in jobs)
     cpu_model = ""
@@ -634,6 +682,7 @@ def main():
     if not args.no_legs:
         for name, f in (("conv", bench_conv), ("snapshot_copy", bench_snapshot),
                         ("prefix_cache_host", bench_prefix_cache), ("decode", bench_decode),
+                        ("decode_conv", bench_decode_conv),
                         ("decode_tokens", bench_decode_tokens),
                         ("mixed", bench_mixed), ("overlap", bench_overlap)):
             log(f"[bench] leg {name}")
@@ -672,6 +721,7 @@ def main():
         "data": "synthetic (seeded; shapes of the pages' chat waves)",
         "config": {"workload": head["workload"], "tokens": p.n_tokens, "prompts": p.n_seqs,
                    "qk_heads": p.Hqk, "v_heads": p.Hv, "head_dim": p.dk, "chunk": p.chunk,
+                   "kernel_chunk": kernel_chunk(p),
                    "checkpoint_block": p.block, "checkpoints": head["checkpoints"],
                    "timing": ("K steps queued back to back between two device synchronisations, "
                               "each step's checkpoint copy on its own stream right after its scan, "
@@ -680,7 +730,9 @@ def main():
                               "region / K" if args.workload == "chat" else
                               "median of per-launch HIP-event times on the launch stream; 1 GiB "
                               "cache flush before each launch, outside the events"),
-                   "wall_s_timed_region": t_wall},
+                   "wall_s_timed_region": (head["step"]["region_wall_ms"] * 1e-3 if head.get("step")
+                                           else head["wall_ms_timed"] * 1e-3),
+                   "wall_s_all_legs_of_headline": t_wall},
         "step": head.get("step"),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -688,6 +740,15 @@ def main():
                      "kernel": "pipelined_prefill_kernel<128,128>", "alg_bytes_per_launch": head["alg_bytes"],
                      "launch_ms_mean": head["scan_ms_mean"],
                      "mfma_alg_tflops": head["alg_flops"] / mean_s / 1e12},
+        "step_roofline": ({"bound": "hbm", "alg_bytes_min": head["step"]["step_min_bytes"],
+                           "achieved": head["step"]["step_min_bytes"] / (head["ms_median"] * 1e-3) / 1e9,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": head["step"]["step_min_bytes"] / (head["ms_median"] * 1e-3) / 1e9
+                           / HBM_PEAK_GBS,
+                           "note": "whole step (conv, scan, checkpoint copy) against the fewest bytes "
+                                   "one pass can move: x, g, beta in, out, final states and "
+                                   "checkpoints once, conv weights and states"}
+                          if head.get("step") else None),
         "cpu_baseline": cpu,
         "legs": legs,
         "step_ms_p10_p90": [head["ms_p10"], head["ms_p90"]],

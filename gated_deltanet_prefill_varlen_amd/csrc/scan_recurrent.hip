@@ -139,9 +139,8 @@ recurrent_prefill_kernel(const ScanArgs a) {
 // group rg, lane part jl) holds its 16 entries of rows rg, rg + 32, ...
 // (RPT rows), so it keeps several state rows in flight and forms k, q and
 // their norms once for them.  Each row's arithmetic is that of token_step.
-template <int DK, int DV, int RPT, typename IO>
-__global__ void __launch_bounds__(kRows * (DK / 16))
-decode_kernel(const DecodeArgs a) {
+template <int DK, int DV, int RPT, typename IO, bool CONV>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   constexpr int LPR = DK / 16;
   using T = typename IO::T;
   const int b = blockIdx.x, h = blockIdx.y;
@@ -152,52 +151,57 @@ decode_kernel(const DecodeArgs a) {
   // a token's inputs do not depend on the slot: without the conv, token 0's
   // are requested before the slot -> state address round trip
   float kv[16], qv[16], vrow[RPT], galpha, gbeta;
-  const bool conv = a.conv_w != nullptr;
   int r = 0;
   // With the conv, q, k and v are its inputs: the value of channel c at token
   // n is conv4_silu over the channel's inputs at n-3 .. n (before the
   // sequence's first token, its slot's conv state), rounded to the io dtype
-  // as a stored conv output would be (channels ordered q | k | v).
+  // as a stored conv output would be (channels ordered q | k | v).  The
+  // workgroup computes each channel it needs once (k and q of its qk head,
+  // v of its rows) into LDS, then every thread reads its values back.
   const T* cst = static_cast<const T*>(a.conv_state);
-  auto conv_in4 = [&](const T* x, int64_t stride, int p, int ch, float* out) {
-    if (p >= 0) load4<IO>(x + ((size_t)b * a.n_tok + p) * stride, out);
-    else load4<IO>(cst + ((size_t)r * 3 + 3 + p) * a.conv_dim + ch, out);
-  };
-  auto conv_row16 = [&](const T* x, int64_t stride, int ch0, int n, float* out) {
+  constexpr int NCH = 2 * DK + kRows * RPT;   // k, q, v channels of this workgroup
+  __shared__ float conv_out[CONV ? NCH : 1];
+  auto conv_token = [&](int n) __attribute__((always_inline)) {
+    const int nq = a.Hqk * DK;
+    __syncthreads();   // the previous token's values have been read
+    for (int e = tid; e < NCH; e += kRows * LPR) {
+      const T* x;
+      int64_t stride;
+      int ch;
+      if (e < DK) { x = static_cast<const T*>(a.k) + j * DK + e; stride = a.k_stride; ch = nq + j * DK + e; }
+      else if (e < 2 * DK) { x = static_cast<const T*>(a.q) + j * DK + e - DK; stride = a.q_stride; ch = j * DK + e - DK; }
+      else {
+        const int col = h * DV + blockIdx.z * kRows * RPT + (e - 2 * DK);   // the workgroup's rows
+        x = static_cast<const T*>(a.v) + col;
+        stride = a.v_stride;
+        ch = 2 * nq + col;
+      }
+      float xw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = 4 * LPR * i + 4 * jl;
-      float xw[4][4];
+      for (int p = 0; p < 4; ++p) {   // one load each, from the token rows or the slot's window
+        const int pp = n - 3 + p;
+        xw[p] = load1<IO>(pp >= 0 ? x + ((size_t)b * a.n_tok + pp) * stride
+                                  : cst + ((size_t)r * 3 + 3 + pp) * a.conv_dim + ch);
+      }
+      const float4 w = reinterpret_cast<const float4*>(a.conv_w)[ch];
+      const float y = conv4_silu(w.x, w.y, w.z, w.w, xw[0], xw[1], xw[2], xw[3]);
+      conv_out[e] = IO::kBytes == 2 ? round_bf16(y) : y;
+    }
+    __syncthreads();
 #pragma unroll
-      for (int p = 0; p < 4; ++p) conv_in4(x + d0, stride, n - 3 + p, ch0 + d0, xw[p]);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float4 w = reinterpret_cast<const float4*>(a.conv_w)[ch0 + d0 + e];
-        const float y = conv4_silu(w.x, w.y, w.z, w.w, xw[0][e], xw[1][e], xw[2][e], xw[3][e]);
-        out[4 * i + e] = IO::kBytes == 2 ? round_bf16(y) : y;
+        kv[4 * i + e] = conv_out[4 * LPR * i + 4 * jl + e];
+        qv[4 * i + e] = conv_out[DK + 4 * LPR * i + 4 * jl + e];
       }
-    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) vrow[i] = conv_out[2 * DK + tid / LPR + kRows * i];
   };
-  auto load_tok = [&](int n) {
+  auto load_tok = [&](int n) __attribute__((always_inline)) {
     const size_t t = (size_t)b * a.n_tok + n;
-    if (conv) {
-      const int nq = a.Hqk * DK;
-      conv_row16(static_cast<const T*>(a.k) + j * DK, a.k_stride, nq + j * DK, n, kv);
-      conv_row16(static_cast<const T*>(a.q) + j * DK, a.q_stride, j * DK, n, qv);
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int col = h * DV + rg + kRows * i, ch = 2 * nq + col;
-        float xw[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int pp = n - 3 + p;
-          xw[p] = pp >= 0 ? load1<IO>(static_cast<const T*>(a.v) + ((size_t)b * a.n_tok + pp) * a.v_stride + col)
-                          : load1<IO>(cst + ((size_t)r * 3 + 3 + pp) * a.conv_dim + ch);
-        }
-        const float4 w = reinterpret_cast<const float4*>(a.conv_w)[ch];
-        const float y = conv4_silu(w.x, w.y, w.z, w.w, xw[0], xw[1], xw[2], xw[3]);
-        vrow[i] = IO::kBytes == 2 ? round_bf16(y) : y;
-      }
+    if constexpr (CONV) {
+      conv_token(n);
     } else {
       load_row16<LPR, IO>(static_cast<const T*>(a.k) + t * a.k_stride + j * DK, jl, kv);
       load_row16<LPR, IO>(static_cast<const T*>(a.q) + t * a.q_stride + j * DK, jl, qv);
@@ -208,7 +212,7 @@ decode_kernel(const DecodeArgs a) {
     galpha = a.g[t * a.Hv + h];
     gbeta = a.beta[t * a.Hv + h];
   };
-  if (conv) {
+  if constexpr (CONV) {   // token 0's window reaches into the slot's conv state
     r = a.slot ? a.slot[b] : b;
     load_tok(0);
   } else {
@@ -236,6 +240,16 @@ decode_kernel(const DecodeArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) store_row16f<LPR>(sp + (size_t)(rg + kRows * i) * DK, jl, S[i]);
+}
+
+template <int DK, int DV, int RPT, typename IO>
+__global__ void __launch_bounds__(kRows * (DK / 16)) decode_kernel(const DecodeArgs a) {
+  decode_body<DK, DV, RPT, IO, false>(a);
+}
+
+template <int DK, int DV, int RPT, typename IO>
+__global__ void __launch_bounds__(kRows * (DK / 16)) decode_conv_kernel(const DecodeArgs a) {
+  decode_body<DK, DV, RPT, IO, true>(a);
 }
 
 // The conv state of each decoding sequence's slot moves on by n_tok inputs:
@@ -282,13 +296,18 @@ hipError_t launch_dec(const DecodeArgs& a, hipStream_t st) {
   // k/q loads and norms of each token shared by them (decode of 32 x 4
   // tokens 96 -> 81 us)
   constexpr int RPT = DV / kRows < 4 ? DV / kRows : 4;
-  if (a.n_tok == 1) {
-    constexpr int R1 = DV / kRows < 2 ? DV / kRows : 2;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, R1, IO>), dim3(a.batch, a.Hv, DV / (kRows * R1)), dim3(kRows * (DK / 16)),
-                       0, st, a);
+  constexpr int R1 = DV / kRows < 2 ? DV / kRows : 2;
+  const dim3 blk(kRows * (DK / 16));
+  if (a.conv_w) {
+    if (a.n_tok == 1)
+      hipLaunchKernelGGL((decode_conv_kernel<DK, DV, R1, IO>), dim3(a.batch, a.Hv, DV / (kRows * R1)), blk, 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_conv_kernel<DK, DV, RPT, IO>), dim3(a.batch, a.Hv, DV / (kRows * RPT)), blk, 0, st,
+                         a);
+  } else if (a.n_tok == 1) {
+    hipLaunchKernelGGL((decode_kernel<DK, DV, R1, IO>), dim3(a.batch, a.Hv, DV / (kRows * R1)), blk, 0, st, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<DK, DV, RPT, IO>), dim3(a.batch, a.Hv, DV / (kRows * RPT)),
-                       dim3(kRows * (DK / 16)), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<DK, DV, RPT, IO>), dim3(a.batch, a.Hv, DV / (kRows * RPT)), blk, 0, st, a);
   }
   if (a.conv_w) {
     const hipError_t e = hipGetLastError();

@@ -2,6 +2,9 @@
 through its C ABI, run the oracle on the same inputs, compare."""
 from __future__ import annotations
 
+import multiprocessing as mp
+import os
+
 import numpy as np
 import torch
 
@@ -127,3 +130,73 @@ def sample_pairs(p: W.Pack, n: int, seed: int = 0):
     while len(pairs) < min(n, p.n_seqs * p.Hv):
         pairs.add((int(rng.integers(p.n_seqs)), int(rng.integers(p.Hv))))
     return sorted(pairs)
+
+
+# ------------------------------------------- many pairs in a process pool --
+
+def _oracle_job(job):
+    """One (prompt, head) on the oracle: optional conv (its output rounded to
+    bf16 as the GPU tensor stores it), then the token-by-token recurrence."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        q, k, v, g, b, init, mine, scale, xs, w, d = job
+        if xs is not None:
+            ys = O.round_bf16(O.conv1d_silu_packed(xs, w, [0, xs.shape[0]])[0])
+            q, k, v = ys[:, None, :d], ys[:, None, d:2 * d], ys[:, None, 2 * d:]
+        out, fin, ck = O.prefill_recurrent(q, k, v, g, b, [0, q.shape[0]], init=init,
+                                           ckpt_positions=mine, scale=scale)
+        return out[:, 0], fin[0, 0], ck[:, 0]
+
+
+def oracle_pairs(p: W.Pack, pairs, ckpt=(), conv=False, g=None, beta=None, procs=None):
+    """The oracle on many (prompt, head) pairs of a pack, one process per host
+    core (at most 16), each job holding only its prompt's slices.  With conv,
+    q, k, v come from the pack's pre-conv rows x and conv weights.  Returns a
+    list of (out [L, dv], final [dv, dk], ckpts [n, dv, dk])."""
+    g = p.g if g is None else g
+    beta = p.beta if beta is None else beta
+    cu = p.cu_seqlens
+    d = p.dk
+    jobs = []
+    for s, h in pairs:
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        j = h // (p.Hv // p.Hqk)
+        init = None if p.init is None else p.init[s:s + 1, h:h + 1].astype(np.float64)
+        mine = [int(x) - c0 for x in ckpt if c0 < x <= c1]
+        gb = (g[c0:c1, h:h + 1].astype(np.float64), beta[c0:c1, h:h + 1].astype(np.float64))
+        if conv:
+            chans = np.r_[j * d:(j + 1) * d, p.Hqk * d + j * d:p.Hqk * d + (j + 1) * d,
+                          2 * p.Hqk * d + h * p.dv:2 * p.Hqk * d + (h + 1) * p.dv]
+            jobs.append((None, None, None) + gb + (init, mine, p.scale, O.to_f64(p.x[c0:c1][:, chans], p.dtype),
+                                                   p.conv_w[chans].astype(np.float64), d))
+        else:
+            jobs.append((O.to_f64(p.q[c0:c1, j:j + 1], p.dtype), O.to_f64(p.k[c0:c1, j:j + 1], p.dtype),
+                         O.to_f64(p.v[c0:c1, h:h + 1], p.dtype)) + gb + (init, mine, p.scale, None, None, d))
+    procs = procs or max(1, min(16, len(os.sched_getaffinity(0)), len(jobs)))
+    if procs == 1:
+        return [_oracle_job(j) for j in jobs]
+    with mp.get_context("spawn").Pool(procs) as pool:
+        res = pool.map(_oracle_job, jobs)
+        pool.close()
+        pool.join()
+    return res
+
+
+def compare_pairs(p: W.Pack, pairs, refs, out, final, ckpt_buf, ckpt=()):
+    """Element-by-element comparison of GPU results (host fp64 arrays: out
+    [T, Hv, dv], final [N, Hv, dv, dk], ckpt_buf [n, Hv, dv, dk]) with oracle
+    results for the pairs; asserts the tolerances, returns the worst errors."""
+    tol_o = OUT_TOL[p.dtype]
+    cu = p.cu_seqlens
+    worst_o = worst_s = 0.0
+    for (s, h), (ro, rf, rc) in zip(pairs, refs):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        eo = float(np.max(O.max_rel_rows(out[c0:c1, h], ro))) if c1 > c0 else 0.0
+        es = float(O.rel_frobenius(final[s, h], rf))
+        idx = [i for i, x in enumerate(ckpt) if c0 < x <= c1]
+        for n, i in enumerate(idx):
+            es = max(es, float(O.rel_frobenius(ckpt_buf[i, h], rc[n])))
+        assert eo <= tol_o, f"output rel err {eo:.3e} > {tol_o} at seq {s} head {h}"
+        assert es <= STATE_TOL, f"state rel err {es:.3e} > {STATE_TOL} at seq {s} head {h}"
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+    return worst_o, worst_s

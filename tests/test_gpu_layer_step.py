@@ -6,7 +6,7 @@ device pool on its own stream.  Two steps run as consecutive layers: each
 step's copy waits for an event from its scan and runs beside the next step's
 work, the two steps writing alternate checkpoint buffers (the second with
 other gates, so that a copy of the wrong buffer shows).  The second step is checked against the oracle's conv followed by
-its token-by-token recurrence on sampled (prompt, head) pairs (the conv
+its token-by-token recurrence on 64 sampled (prompt, head) pairs (the conv
 output rounded to bf16 as the tensor stores it); conv states, windows and
 both pools are bit-exact (they are copies).
 
@@ -17,9 +17,9 @@ import pytest
 import torch
 
 import gated_deltanet_prefill_varlen_amd as gdn
-import oracle as O
 import workloads as W
-from gpu_util import DEV, STATE_TOL, OUT_TOL, io_tensor, f32_tensor, i32_tensor, sample_pairs, to_f64
+from gpu_util import (DEV, compare_pairs, io_tensor, f32_tensor, i32_tensor, oracle_pairs, sample_pairs,
+                      to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,25 +77,7 @@ def test_layer_step_chat_wave_sampled():
     for i, c in enumerate(ck):   # conv windows: the three inputs before each checkpoint
         assert torch.equal(conv_ckpt[i].cpu(), xb[int(c) - 3:int(c)])
 
-    worst_o = worst_s = 0.0
-    for s, h in sample_pairs(p, 6, seed=5):
-        j = h // (Hv // Hqk)
-        c0, c1 = int(cu[s]), int(cu[s + 1])
-        chans = np.r_[j * d:(j + 1) * d, Hqk * d + j * d:Hqk * d + (j + 1) * d,
-                      2 * Hqk * d + h * d:2 * Hqk * d + (h + 1) * d]
-        xs = O.to_f64(p.x[c0:c1][:, chans], "bf16")
-        ys = O.round_bf16(O.conv1d_silu_packed(xs, p.conv_w[chans].astype(np.float64), [0, c1 - c0])[0])
-        q, k, v = ys[:, None, :d], ys[:, None, d:2 * d], ys[:, None, 2 * d:]
-        mine = [int(c) - c0 for c in ck if c0 < c <= c1]
-        ro, rf, rc = O.prefill_recurrent(q, k, v, g_np[c0:c1, h:h + 1].astype(np.float64),
-                                         beta_np[c0:c1, h:h + 1].astype(np.float64), [0, c1 - c0],
-                                         ckpt_positions=mine)
-        eo = float(np.max(O.max_rel_rows(to_f64(out[c0:c1, h]), ro[:, 0])))
-        es = float(O.rel_frobenius(to_f64(final[s, h]), rf[0, 0]))
-        idx = [i for i, c in enumerate(ck) if c0 < c <= c1]
-        for n, i in enumerate(idx):
-            es = max(es, float(O.rel_frobenius(to_f64(ckbuf[i, h]), rc[n, 0])))
-        assert eo <= OUT_TOL["bf16"], f"output rel err {eo:.3e} at seq {s} head {h}"
-        assert es <= STATE_TOL, f"state rel err {es:.3e} at seq {s} head {h}"
-        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+    pairs = sample_pairs(p, 64, seed=5)
+    refs = oracle_pairs(p, pairs, ck, conv=True, g=g_np, beta=beta_np)
+    worst_o, worst_s = compare_pairs(p, pairs, refs, to_f64(out), to_f64(final), to_f64(ckbuf), ck)
     print(f"layer step: out {worst_o:.2e} state {worst_s:.2e}")

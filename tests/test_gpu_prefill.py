@@ -10,8 +10,8 @@ import torch
 import gated_deltanet_prefill_varlen_amd as gdn
 import oracle as O
 import workloads as W
-from gpu_util import (DevPack, all_pairs, assert_parity, sample_pairs, shape_of, to_f64,
-                      io_tensor, f32_tensor, i32_tensor, DEV)
+from gpu_util import (DevPack, all_pairs, assert_parity, compare_pairs, oracle_pairs, sample_pairs,
+                      shape_of, to_f64, io_tensor, f32_tensor, i32_tensor, DEV)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,25 +167,31 @@ def test_ragged_packed_equals_alone_bitwise(seed):
     assert_parity(dp, sample_pairs(p, 24, seed=seed))
 
 
-@pytest.mark.slow
-def test_chat_wave_full_size_sampled():
-    p = W.chat_wave()
+def _full_size(p, pairs):
     ck = _ckpt(p)
-    assert len(ck) == 96
     dp = DevPack(p, ck).run()
     torch.cuda.synchronize()
-    eo, es = assert_parity(dp, sample_pairs(p, 8))
+    refs = oracle_pairs(p, pairs, ck)
+    ck_np = to_f64(dp.ckpt_buf) if dp.ckpt_buf is not None else None
+    return ck, compare_pairs(p, pairs, refs, to_f64(dp.out), to_f64(dp.final), ck_np, ck)
+
+
+@pytest.mark.slow
+def test_chat_wave_full_size_sampled():
+    """64 of the 1,024 (prompt, head) pairs, every output row and checkpoint
+    of each, in the launch configuration the benchmark times."""
+    p = W.chat_wave()
+    ck, (eo, es) = _full_size(p, sample_pairs(p, 64))
+    assert len(ck) == 96
     print(f"chat wave: out {eo:.2e} state {es:.2e}")
 
 
 @pytest.mark.slow
-def test_long_prompts_full_size_sampled():
+def test_long_prompts_full_size_all_pairs():
+    """All 128 (prompt, head) pairs of the 4 x 8,192-token pack."""
     p = W.long_prompts()
-    ck = _ckpt(p)
+    ck, (eo, es) = _full_size(p, all_pairs(p))
     assert len(ck) == 28
-    dp = DevPack(p, ck).run()
-    torch.cuda.synchronize()
-    eo, es = assert_parity(dp, sample_pairs(p, 3, seed=4))
     print(f"long prompts: out {eo:.2e} state {es:.2e}")
 
 
