@@ -206,7 +206,7 @@ def conv_alg_bytes(T: int, N: int, C: int, n_ckpt: int, e: int = 2) -> int:
     return 2 * T * C * e + C * 4 * 4 + (N + n_ckpt) * 3 * C * e
 
 
-def bench_layer_step(torch, gdn, p, steps, warmup, stream, label):
+def bench_layer_step(torch, gdn, p, steps, warmup, stream, label, fused=False):
     """One step is one pass of the whole hot path over the chat wave: the
     packed conv1d + SiLU from the pre-conv rows x into one [T, conv_dim]
     tensor (with the prompts' conv states and the conv windows at the
@@ -222,7 +222,10 @@ def bench_layer_step(torch, gdn, p, steps, warmup, stream, label):
     copy joined before its closing event.  Inside it only the scan carries
     events (its own time, for its roofline); a second region of K steps with
     events around each conv as well gives the breakdown (each event pair
-    costs a few microseconds, so that region is not the headline)."""
+    costs a few microseconds, so that region is not the headline).  With
+    ``fused`` the conv and the scan are one gdn_prefill_conv_packed call (the
+    conv in the scan's loads; the same conv states and windows), timed as
+    "scan"."""
     T, N = p.n_tokens, p.n_seqs
     C = 2 * p.Hqk * p.dk + p.Hv * p.dv
     ck = gdn.gdn_plan_checkpoints(p.cu_seqlens, p.block)
@@ -261,14 +264,20 @@ def bench_layer_step(torch, gdn, p, steps, warmup, stream, label):
             stream.wait_event(copy_done[b])
             if e and conv_events:
                 e[0].record(stream)
-            gdn.gdn_conv1d_silu_packed(shape, cu_d, p.cu_seqlens, x, w, y, None, conv_state, ck_d, ck,
-                                       conv_ckpt, stream=stream)
+            if not fused:
+                gdn.gdn_conv1d_silu_packed(shape, cu_d, p.cu_seqlens, x, w, y, None, conv_state, ck_d, ck,
+                                           conv_ckpt, stream=stream)
             if e and conv_events:
                 e[1].record(stream)
             if e:
                 e[2].record(stream)
-            gdn.gdn_prefill_packed(shape, cu_d, p.cu_seqlens, qv, kv, vv, g, beta, None, ck_d, ck,
-                                   out, final, ckbufs[b], stream=stream)
+            if fused:
+                gdn.gdn_prefill_conv_packed(shape, cu_d, p.cu_seqlens, x, w, g, beta, None, ck_d, ck, out,
+                                            final, ckbufs[b], conv_state_out=conv_state,
+                                            conv_ckpt=conv_ckpt, stream=stream)
+            else:
+                gdn.gdn_prefill_packed(shape, cu_d, p.cu_seqlens, qv, kv, vv, g, beta, None, ck_d, ck,
+                                       out, final, ckbufs[b], stream=stream)
             # one event marks the scan's end, for its timing and for the copy
             done = e[3] if e else scan_done[b]
             done.record(stream)
@@ -314,7 +323,7 @@ def bench_layer_step(torch, gdn, p, steps, warmup, stream, label):
                              "conv_ms_median": statistics.median(conv_ms),
                              "scan_ms_median": statistics.median(scan_b_ms)},
         "scan_alg_bytes": B_scan, "scan_alg_flops": F,
-        "step_alg_bytes": B_scan + B_conv + B_copy,
+        "step_alg_bytes": (step_min_bytes(p, n_ck) + B_copy) if fused else B_scan + B_conv + B_copy,
         "step_min_bytes": step_min_bytes(p, n_ck),
         "copy_exact": exact,
     }
@@ -688,6 +697,13 @@ def main():
             log(f"[bench] leg {name}")
             legs[name] = f(torch, gdn, stream, flush, 10)
         if args.workload == "chat":
+            log("[bench] leg step_conv_fused")
+            legs["step_conv_fused"] = bench_layer_step(
+                torch, gdn, p, args.steps, args.warmup, stream,
+                makers["chat"][1] + ": the conv fused into the scan's loads (one launch), checkpoint copy "
+                "on its own stream", fused=True)
+            legs["step_conv_fused"]["vs_two_launches"] = (legs["step_conv_fused"]["ms_per_step"] /
+                                                          head["ms_median"])
             log("[bench] leg scan_only")
             legs["scan_only"], _ = bench_prefill(torch, gdn, p, args.steps, args.warmup, stream, flush,
                                                  makers["chat"][1] + ", scan alone (dense q, k, v)")

@@ -22,8 +22,8 @@ import torch
 
 __all__ = [
     "GdnError", "gdn_shape", "make_shape", "load", "GDN_BF16", "GDN_F32", "GDN_QK_L2NORM",
-    "gdn_status_string", "gdn_plan_checkpoints", "gdn_prefill_packed", "gdn_decode_step",
-    "gdn_decode_tokens",
+    "gdn_status_string", "gdn_plan_checkpoints", "gdn_prefill_packed", "gdn_prefill_conv_packed",
+    "gdn_decode_step", "gdn_decode_tokens",
     "gdn_conv1d_silu_packed", "gdn_snapshot_copy", "LIB_PATH", "EXPORTED",
 ]
 
@@ -33,7 +33,8 @@ GDN_QK_L2NORM = 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_SEQLENS", 5: "GDN_ERR_CKPT", 6: "GDN_ERR_CAPACITY", 7: "GDN_ERR_HIP"}
 EXPORTED = ("gdn_status_string", "gdn_plan_checkpoints", "gdn_conv1d_silu_packed",
-            "gdn_prefill_packed", "gdn_decode_step", "gdn_decode_tokens", "gdn_snapshot_copy")
+            "gdn_prefill_packed", "gdn_prefill_conv_packed", "gdn_decode_step",
+            "gdn_decode_tokens", "gdn_snapshot_copy")
 
 
 class GdnError(RuntimeError):
@@ -83,6 +84,9 @@ def load() -> ctypes.CDLL:
     lib.gdn_prefill_packed.restype = _I32
     lib.gdn_prefill_packed.argtypes = [_SP, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _I32, _P, _P, _P, _P]
+    lib.gdn_prefill_conv_packed.restype = _I32
+    lib.gdn_prefill_conv_packed.argtypes = [_SP, _P, _P, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P,
+                                            _P, _P, _P, _I32, _P, _P, _P, _P, _P]
     lib.gdn_decode_step.restype = _I32
     lib.gdn_decode_step.argtypes = [_SP, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P]
     lib.gdn_decode_tokens.restype = _I32
@@ -197,6 +201,24 @@ def gdn_prefill_packed(shape: gdn_shape, cu_seqlens, cu_seqlens_host, q, k, v, g
         _dev(q), _dev(k), _dev(v), _dev(g), _dev(beta), _dev(init_state),
         _dev(ckpt_positions), _hp(ck_h), n_ckpt, _dev(out), _dev(final_state), _dev(ckpt_buf),
         _stream(stream)), "gdn_prefill_packed")
+
+
+def gdn_prefill_conv_packed(shape: gdn_shape, cu_seqlens, cu_seqlens_host, x, conv_weight, g,
+                            beta, init_state, ckpt_positions, ckpt_positions_host, out,
+                            final_state, ckpt_buf, conv_state_in=None, conv_state_out=None,
+                            conv_ckpt=None, x_tok_stride: int = 0, stream=None) -> None:
+    """The packed prefill reading pre-conv rows x (the short conv fused into
+    the scan's loads)."""
+    cu_h = _host_i32(cu_seqlens_host)
+    ck_h = _host_i32(ckpt_positions_host)
+    n_ckpt = 0 if ck_h is None else len(ck_h)
+    n_tokens = int(cu_h[-1]) if len(cu_h) else 0
+    _check(load().gdn_prefill_conv_packed(
+        ctypes.byref(shape), _dev(cu_seqlens), _hp(cu_h), len(cu_h) - 1, n_tokens,
+        _dev(x), x_tok_stride, _dev(conv_weight), _dev(conv_state_in), _dev(conv_state_out),
+        _dev(g), _dev(beta), _dev(init_state), _dev(ckpt_positions), _hp(ck_h), n_ckpt,
+        _dev(conv_ckpt), _dev(out), _dev(final_state), _dev(ckpt_buf), _stream(stream)),
+        "gdn_prefill_conv_packed")
 
 
 def gdn_decode_step(shape: gdn_shape, q, k, v, g, beta, state, slot=None, slot_host=None,

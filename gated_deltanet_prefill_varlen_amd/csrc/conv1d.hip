@@ -171,6 +171,25 @@ __global__ void __launch_bounds__(kThreads) conv_state_kernel(const ConvArgs a) 
   copy_window<IO>(a, sq, a.cu[sq + 1], static_cast<typename IO::T*>(a.state_out) + (size_t)sq * 3 * a.conv_dim, c0);
 }
 
+// Each prompt's last three inputs to state_out (reading its history from
+// state_in, which state_out may be), one block row per prompt.
+template <typename IO>
+hipError_t launch_states(const ConvArgs& a, hipStream_t st) {
+  const int gc = (a.conv_dim / kVec + kThreads - 1) / kThreads;
+  for (int s0 = 0; s0 < a.n_seqs; s0 += 65535) {
+    ConvArgs b = a;
+    b.cu = a.cu + s0;
+    b.n_seqs = a.n_seqs - s0;
+    if (a.state_in)
+      b.state_in = static_cast<const char*>(a.state_in) + (size_t)s0 * 3 * a.conv_dim * IO::kBytes;
+    b.state_out = static_cast<char*>(a.state_out) + (size_t)s0 * 3 * a.conv_dim * IO::kBytes;
+    hipLaunchKernelGGL(conv_state_kernel<IO>, dim3(gc, min(65535, a.n_seqs - s0)), dim3(kThreads), 0, st, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <typename IO>
 hipError_t launch(const ConvArgs& a, hipStream_t st) {
   constexpr int kS = RawRow<IO>::kStrip;
@@ -189,23 +208,17 @@ hipError_t launch(const ConvArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  for (int s0 = 0; in_place && s0 < a.n_seqs; s0 += 65535) {
-    ConvArgs b = a;
-    b.cu = a.cu + s0;
-    b.n_seqs = a.n_seqs - s0;
-    b.state_in = static_cast<const char*>(a.state_in) + (size_t)s0 * 3 * a.conv_dim * IO::kBytes;
-    b.state_out = static_cast<char*>(a.state_out) + (size_t)s0 * 3 * a.conv_dim * IO::kBytes;
-    hipLaunchKernelGGL(conv_state_kernel<IO>, dim3(gc, min(65535, a.n_seqs - s0)), dim3(kThreads), 0, st, b);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return in_place ? launch_states<IO>(a, st) : hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t st) {
   return a.bf16 ? launch<IoBf16>(a, st) : launch<IoF32>(a, st);
+}
+
+hipError_t launch_conv_states(const ConvArgs& a, hipStream_t st) {
+  return a.bf16 ? launch_states<IoBf16>(a, st) : launch_states<IoF32>(a, st);
 }
 
 }  // namespace gdn

@@ -175,6 +175,72 @@ gdn_status gdn_prefill_packed(const gdn_shape* shape, const int32_t* cu_seqlens,
   return finish_launch(gdn::launch_prefill(a, s), s);
 }
 
+gdn_status gdn_prefill_conv_packed(const gdn_shape* shape, const int32_t* cu_seqlens,
+                                   const int32_t* cu_seqlens_host, int32_t n_seqs, int32_t n_tokens,
+                                   const void* x, int64_t x_tok_stride, const float* conv_weight,
+                                   const void* conv_state_in, void* conv_state_out, const float* g,
+                                   const float* beta, const float* init_state,
+                                   const int32_t* ckpt_positions, const int32_t* ckpt_positions_host,
+                                   int32_t n_ckpt, void* conv_ckpt, void* out, float* final_state,
+                                   float* ckpt_buf, void* stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  // the kernel that fuses the conv: bf16, d_k = d_v = 128, 32-token tiles
+  if (shape->io_dtype != GDN_BF16 || shape->head_k_dim != 128 || shape->head_v_dim != 128 ||
+      shape->chunk < 32)
+    return GDN_ERR_UNSUPPORTED;
+  st = check_seqlens(cu_seqlens_host, n_seqs, n_tokens);
+  if (st != GDN_OK) return st;
+  if (n_seqs > 0 && (!cu_seqlens || !conv_weight)) return GDN_ERR_NULL;
+  if (n_tokens > 0 && (!x || !g || !beta || !out)) return GDN_ERR_NULL;
+  if (n_ckpt < 0) return GDN_ERR_SHAPE;
+  if (n_ckpt > 0 && (!ckpt_positions || !ckpt_positions_host || !ckpt_buf)) return GDN_ERR_NULL;
+  st = check_ckpts(cu_seqlens_host, n_seqs, ckpt_positions_host, n_ckpt);
+  if (st != GDN_OK) return st;
+  const int64_t Hqk = shape->num_qk_heads, Hv = shape->num_v_heads;
+  const int64_t conv_dim = 2 * Hqk * 128 + Hv * 128;
+  int64_t xs;
+  if ((st = resolve_stride(shape, x_tok_stride, conv_dim, &xs)) != GDN_OK) return st;
+  const void* ptrs[] = {x, conv_weight, conv_state_in, conv_state_out, conv_ckpt, out,
+                        init_state, final_state, ckpt_buf};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN_ERR_SHAPE;
+  if (n_tokens > 0) {  // out must not overlap x
+    const char* xb = static_cast<const char*>(x);
+    const char* ob = static_cast<const char*>(out);
+    const char* xe = xb + ((int64_t)(n_tokens - 1) * xs + conv_dim) * 2;
+    const char* oe = ob + (int64_t)n_tokens * Hv * 128 * 2;
+    if (xb < oe && ob < xe) return GDN_ERR_SHAPE;
+  }
+  if (n_seqs == 0) return GDN_OK;
+
+  gdn::ScanArgs a{};
+  a.cu = cu_seqlens; a.n_seqs = n_seqs; a.n_tokens = n_tokens;
+  a.g = g; a.beta = beta; a.init = init_state;
+  a.ckpt = ckpt_positions; a.n_ckpt = n_ckpt;
+  a.out = out; a.final_state = final_state; a.ckpt_buf = ckpt_buf;
+  a.Hqk = (int32_t)Hqk; a.Hv = (int32_t)Hv; a.dk = 128; a.dv = 128;
+  a.chunk = shape->chunk; a.bf16 = 1;
+  a.l2norm = (shape->flags & GDN_QK_L2NORM) != 0;
+  a.scale = shape->scale; a.eps = shape->l2_eps;
+  a.conv_x = x; a.conv_x_stride = xs; a.conv_w = conv_weight;
+  a.conv_state_in = conv_state_in; a.conv_state_out = conv_state_out; a.conv_ckpt = conv_ckpt;
+  a.conv_dim = (int32_t)conv_dim;
+  // conv states written in place: every workgroup of a prompt reads its
+  // history first, so the new windows come from a launch of their own after
+  const bool in_place = conv_state_out && conv_state_out == conv_state_in;
+  a.conv_state_own = conv_state_out && !in_place;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gdn::launch_prefill(a, s);
+  if (e == hipSuccess && in_place) {
+    gdn::ConvArgs c{};
+    c.cu = cu_seqlens; c.n_seqs = n_seqs; c.n_tokens = n_tokens; c.conv_dim = (int32_t)conv_dim;
+    c.x = x; c.x_stride = xs; c.state_in = conv_state_in; c.state_out = conv_state_out; c.bf16 = 1;
+    e = gdn::launch_conv_states(c, s);
+  }
+  return finish_launch(e, s);
+}
+
 gdn_status gdn_decode_step(const gdn_shape* shape, int32_t batch, const void* q, const void* k,
                            const void* v, const float* g, const float* beta, float* state,
                            int64_t pool_slots, const int32_t* slot, const int32_t* slot_host,

@@ -27,6 +27,16 @@ struct ScanArgs {
   int32_t bf16;            // io dtype is bf16 (else fp32)
   int32_t l2norm;
   float scale, eps;
+  // the short conv fused into the scan's loads (conv_x non-null): q, k, v
+  // are then unused and come from the pre-conv rows
+  const void* conv_x;      // [T, conv_dim] bf16, token stride conv_x_stride
+  int64_t conv_x_stride;
+  const float* conv_w;     // [conv_dim, 4]
+  const void* conv_state_in;   // [N, 3, conv_dim] or nullptr (zeros)
+  void* conv_state_out;    // [N, 3, conv_dim], written by the scan when conv_state_own
+  void* conv_ckpt;         // [n_ckpt, 3, conv_dim] or nullptr
+  int32_t conv_dim;
+  int32_t conv_state_own;
 };
 
 struct DecodeArgs {
@@ -82,6 +92,7 @@ hipError_t launch_prefill(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_prefill_recurrent(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
+hipError_t launch_conv_states(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_snapshot_copy(const CopyArgs& a, hipStream_t stream);
 
 }  // namespace gdn

@@ -71,7 +71,7 @@ struct PipeCfg {
                 oA % 16 == 0 && oT % 16 == 0, "align");
 };
 
-template <int DK, int DV>
+template <int DK, int DV, bool CONV>
 __global__ void __launch_bounds__(64 * (DV / 32 + 8), 1)
 pipelined_prefill_kernel(const ScanArgs a) {
   using C = PipeCfg<DK, DV>;
@@ -189,6 +189,41 @@ pipelined_prefill_kernel(const ScanArgs a) {
     }
   };
 
+  // One 16-dim piece pc of row t of a q or k tile (bf16 bits, two 8-value
+  // halves) to fp16 at dst (scaled by 2^ax), four values per step; returns
+  // the row's sum of squares (each row's pieces sit on 8 neighbouring lanes).
+  auto convert_piece = [&](const u32x4 (&x)[2], uint16_t* dst, int t, int pc, int ax) {
+    float ss = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2) {
+        float s1;
+        const u32x2 f = bf16x4_to_f16_exp(u32x2{x[hh][2 * w2], x[hh][2 * w2 + 1]}, ax, s1);
+        ss += s1;
+        *reinterpret_cast<u32x2*>(dst + t * LDK + 16 * pc + 8 * hh + 4 * w2) = f;
+        if (ax != 0) __builtin_amdgcn_sched_barrier(0);
+      }
+    return group_sum<8>(ss);
+  };
+  // The piece again when its row's sum of squares ss is outside the band:
+  // scaled by 2^-e (e the binary exponent of the row's largest magnitude,
+  // one tile at a time to bound the registers the rare path holds); ss
+  // becomes the scaled row's, the scaling exponent is returned.
+  auto rescale_piece = [&](const u32x4 (&x)[2], uint16_t* dst, int t, int pc, int n, float& ss) {
+    uint32_t m = 0;   // the row's largest magnitude (bf16 bits)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = bf16_absmax(m, x[hh][i]);
+    m = group_max_u32<8>(fold16(m));
+    const bool ok = ss >= kQkLo && ss <= kQkHi;
+    const int ax = (ok || m == 0 || t >= n) ? 0 : -bf16_exp(m);
+    __builtin_amdgcn_sched_barrier(0);
+    ss = convert_piece(x, dst, t, pc, ax);
+    return ax;
+  };
+
   // ---- a chunk's HBM rows into registers (loader waves), as in
   //      chunked_prefill_kernel: clamped row indices, 32-bit row offsets
   const uint32_t ksb = (uint32_t)a.k_stride * 2, qsb = (uint32_t)a.q_stride * 2;
@@ -273,34 +308,10 @@ pipelined_prefill_kernel(const ScanArgs a) {
       }
       // rows converted as they are, then, when a row of the wave is far
       // from unit length (rare), that tile again with each such row scaled
-      // by 2^a (one tile at a time, four values per step, to bound the
-      // registers the rare path holds)
-      auto convert = [&](const u32x4 (&x)[2], uint16_t* dst, int a) {
-        float ss = 0.f;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int w2 = 0; w2 < 2; ++w2) {
-            float s1;
-            const u32x2 f = bf16x4_to_f16_exp(u32x2{x[hh][2 * w2], x[hh][2 * w2 + 1]}, a, s1);
-            ss += s1;
-            *reinterpret_cast<u32x2*>(dst + t * LDK + 16 * pc + 8 * hh + 4 * w2) = f;
-            if (a != 0) __builtin_amdgcn_sched_barrier(0);
-          }
-        return group_sum<8>(ss);
-      };
+      // by 2^a
+      auto convert = [&](const u32x4 (&x)[2], uint16_t* dst, int ax) { return convert_piece(x, dst, t, pc, ax); };
       auto rescale = [&](const u32x4 (&x)[2], uint16_t* dst, float& ss) {
-        uint32_t m = 0;   // the row's largest magnitude (bf16 bits)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) m = bf16_absmax(m, x[hh][i]);
-        m = group_max_u32<8>(fold16(m));
-        const bool ok = ss >= kQkLo && ss <= kQkHi;
-        const int ax = (ok || m == 0 || t >= n) ? 0 : -bf16_exp(m);
-        __builtin_amdgcn_sched_barrier(0);
-        ss = convert(x, dst, ax);
-        return ax;
+        return rescale_piece(x, dst, t, pc, n, ss);
       };
       float sk = convert(kx, sK, 0), sq = convert(qx, sQ, 0);
       auto off_band = [&](float ss) { return t < n && !(ss >= kQkLo && ss <= kQkHi); };
@@ -349,69 +360,272 @@ pipelined_prefill_kernel(const ScanArgs a) {
     fetch(R);
   };
 
-  // the factor waves' part of interval it: Gram and K Q^T tiles of chunk
-  // it - 1 (waves NSW + NLW, + 1), the substitution of chunk it - 2 (the
-  // other two)
+  // ---- the short conv in the loads (CONV): the loader waves read the
+  //      pre-conv rows x and apply the width-4 causal conv and SiLU.  Loader
+  //      wave lw owns two channels per lane of one tensor for all rows of a
+  //      chunk (lw 0: q of qk head j, 1: k, 2: v of head h), so a channel's
+  //      three earlier inputs are the lane's own earlier rows: carried from
+  //      chunk to chunk, and from the prompt's conv state before its first
+  //      token.  Wave lw 3 loads the gates.  The conv output, rounded to
+  //      bf16 in conv1d_silu's operation order, is written to the ring slot
+  //      as bf16; the Gram and K Q^T waves convert the k and q tiles to fp16
+  //      in place (convert_tile), with the sums and scalings of the unfused
+  //      staging, so the scan sees the values, norms and scales the separate
+  //      conv and scan give.
+  const int lw = wave - NSW;
+  float cw[2][4], cr[3][2];   // the lane's conv weights and last three inputs
+  int xch = 0;                // the lane's first channel
+  bool own_win = false;       // this workgroup writes the lane's conv windows
+  if constexpr (CONV) {
+    if (wave >= NSW && wave < NSW + C::NLW && lw < 3) {
+      xch = (lw == 0 ? j * DK : lw == 1 ? (a.Hqk + j) * DK : 2 * a.Hqk * DK + h * DV) + 2 * lane;
+      // q/k windows once per qk head (by its first value head), v by every head
+      own_win = lw == 2 || h % (a.Hv / a.Hqk) == 0;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const float4 w4 = reinterpret_cast<const float4*>(a.conv_w)[xch + c2];
+        cw[c2][0] = w4.x; cw[c2][1] = w4.y; cw[c2][2] = w4.z; cw[c2][3] = w4.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        uint32_t w = 0;
+        if (a.conv_state_in)
+          w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.conv_state_in) +
+                                                 ((size_t)s * 3 + i) * a.conv_dim + xch);
+        cr[i][0] = __uint_as_float(w << 16);
+        cr[i][1] = __uint_as_float(w & 0xFFFF0000u);
+      }
+    }
+  }
+  // the lane's three carried inputs (exact bf16 values) as a conv window
+  auto write_window = [&](void* dst3) {
+    uint16_t* d = static_cast<uint16_t*>(dst3) + xch;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      *reinterpret_cast<uint32_t*>(d + (size_t)i * a.conv_dim) =
+          (__float_as_uint(cr[i][0]) >> 16) | (__float_as_uint(cr[i][1]) & 0xFFFF0000u);
+  };
+  // One register set of raw rows: as the conv consumes row t of a chunk,
+  // the next chunk's row t is requested into the freed register, so each
+  // row has an interval to arrive and the wave holds one chunk of rows.
+  struct RowsX {
+    uint32_t x[CT];     // the lane's two channels of each row (bf16 pair)
+    float g, b;         // log-gate and beta of token `lane` (wave lw 3)
+    int n, ck;          // the chunk's tokens; the checkpoint it ends at (or -1)
+  };
+  // the walk's next chunk (past the last one: the last again, no checkpoint)
+  auto next_x = [&](int& t0x, int& nx, int& ck_at) {
+    nx = fwalk.next(CT, ckp, a.n_ckpt, t0x, ck_at);
+    if (nx <= 0) { t0x = last_t0; nx = last_n; ck_at = -1; }
+    last_t0 = t0x;
+    last_n = nx;
+  };
+  // row min(t, nx - 1) of the chunk at t0x, the lane's two channels
+  auto xrow = [&](int t0x, int t, int nx) {
+    const char* xb = static_cast<const char*>(a.conv_x) + (size_t)t0x * a.conv_x_stride * 2;
+    return *reinterpret_cast<const uint32_t*>(
+        row(xb, __umul24(min(t, nx - 1), (uint32_t)a.conv_x_stride * 2) + 2 * xch));
+  };
+  auto gates_x = [&](RowsX& R, int t0x, int nx) {
+    const uint32_t tl = min(lane, nx - 1);
+    R.g = a.g[(size_t)t0x * a.Hv + h + __umul24(tl, hv)];
+    R.b = a.beta[(size_t)t0x * a.Hv + h + __umul24(tl, hv)];
+  };
+  auto first_x = [&](RowsX& R) {
+    int t0x, nx, ck_at;
+    next_x(t0x, nx, ck_at);
+    R.n = nx;
+    R.ck = ck_at;
+    if (lw < 3) {
+#pragma unroll
+      for (int t = 0; t < CT; ++t) R.x[t] = xrow(t0x, t, nx);
+    } else {
+      gates_x(R, t0x, nx);
+    }
+  };
+  // the loader waves' part of interval it with the conv: chunk it staged
+  // from R, which takes the rows of chunk it + 1
+  auto load_stage_x = [&](RowsX& R, int it) {
+    int t0n, nn, ckn;
+    next_x(t0n, nn, ckn);
+    const int cs = it;
+    if (cs < nch) {
+      const int n = R.n;
+      float* sc = ringSc(cs);
+      uint32_t vm = 0;
+      if (lw < 3) {
+        uint16_t* dst = lw == 0 ? ringQ(cs) : lw == 1 ? ringK(cs) : ringV(cs);
+        uint32_t* dcol = reinterpret_cast<uint32_t*>(dst) + lane;
+        const int ldw = (lw == 2 ? LDV : LDK) / 2;
+        // row t of the chunk: conv + SiLU from the carried inputs, the next
+        // chunk's row t requested into the freed register
+        auto conv_row = [&](int t, bool valid) {
+          uint32_t o = 0;   // rows past n: zeros
+          if (valid) {
+            const float x0 = __uint_as_float(R.x[t] << 16), x1 = __uint_as_float(R.x[t] & 0xFFFF0000u);
+            const float y0 = conv4_silu(cw[0][0], cw[0][1], cw[0][2], cw[0][3], cr[0][0], cr[1][0], cr[2][0], x0);
+            const float y1 = conv4_silu(cw[1][0], cw[1][1], cw[1][2], cw[1][3], cr[0][1], cr[1][1], cr[2][1], x1);
+            cr[0][0] = cr[1][0]; cr[0][1] = cr[1][1];
+            cr[1][0] = cr[2][0]; cr[1][1] = cr[2][1];
+            cr[2][0] = x0; cr[2][1] = x1;
+            o = pack_bf16(y0, y1);
+          }
+          R.x[t] = xrow(t0n, t, nn);
+          dcol[t * ldw] = o;
+          vm = bf16_absmax(vm, o);   // used by the v wave
+          asm volatile("" : "+v"(vm));   // taken here: deferred, it keeps every row's output live
+        };
+        if (n == CT) {   // a whole chunk: no branches, the rows interleave
+#pragma unroll
+          for (int t = 0; t < CT; ++t) {
+            conv_row(t, true);
+            if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // four rows in flight
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < CT; ++t) conv_row(t, t < n);
+        }
+        if (own_win) {
+          if (R.ck >= 0 && a.conv_ckpt) write_window(static_cast<uint16_t*>(a.conv_ckpt) + (size_t)R.ck * 3 * a.conv_dim);
+          if (cs == nch - 1 && a.conv_state_own)
+            write_window(static_cast<uint16_t*>(a.conv_state_out) + (size_t)s * 3 * a.conv_dim);
+        }
+        if (lw == 2) vm = wave_max_u32(fold16(vm));
+      } else {   // betas and the base-2 cumsum of the log-gates
+        const float xg = scan32(lane < n ? R.g : 0.f) * 1.44269504088896341f;
+        if (lane < CT) {
+          sc[SC_G * CT + lane] = xg;
+          sc[SC_BETA * CT + lane] = lane < n ? R.b : 0.f;
+        }
+        if (lane == 0) reinterpret_cast<int*>(sc)[SC_VM * CT + 4] = n;   // for the factor waves
+        gates_x(R, t0n, nn);
+      }
+      // the chunk's largest |v| (bf16 bits): the v wave's, zeros beside it
+      if (lane == 0) reinterpret_cast<uint32_t*>(sc)[SC_VM * CT + lw] = lw == 2 ? vm : 0u;
+    }
+    R.n = nn;
+    R.ck = ckn;
+  };
+
+  // A staged bf16 q or k tile of n rows to fp16 in place (CONV), eight rows
+  // per pass with the unfused staging's lane layout (lane 8 r + pc: piece pc
+  // of row r), pieces, sums and scalings, so the values and the row factors
+  // rf[t] are the unfused kernel's.
+  auto convert_tile = [&](uint16_t* sT, float* rf, int n) {
+#pragma unroll 1
+    for (int p8 = 0; p8 < CT / 8; ++p8) {
+      const int t = 8 * p8 + lane / 8, pc = lane % 8;
+      u32x4 x[2];   // 8-byte reads: rows are 8-byte aligned
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(sT + t * LDK + 16 * pc + 8 * hh);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(sT + t * LDK + 16 * pc + 8 * hh + 4);
+        x[hh] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      float ss = convert_piece(x, sT, t, pc, 0);
+      int ax = 0;
+      if (__builtin_amdgcn_ballot_w64(t < n && !(ss >= kQkLo && ss <= kQkHi)))   // rare
+        ax = rescale_piece(x, sT, t, pc, n, ss);
+      if (pc == 7) rf[t] = t < n ? row_factor(a.l2norm, ss, ax, a.eps) : 1.0f;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the fp16 rows written before the wave reads them
+  };
+  auto chunk_n = [&](const float* sc) { return reinterpret_cast<const int*>(sc)[SC_VM * CT + 4]; };
+
+  // A[t][i] = beta_t r_t r_i e^{G_t - G_i} k_t.k_i (i < t) of chunk cg,
+  // stored transposed with rows interleaved over the substitution's lane
+  // parts, and the state path's per-token factors (with CONV the k tile is
+  // converted to fp16 here first)
+  auto gram = [&](int cg) {
+    uint16_t* sK = ringK(cg);
+    float* sc = ringSc(cg);
+    float* sA = bufA(cg);
+    f32x16 acc;
+    if constexpr (CONV) {
+      convert_tile(sK, sc + SC_RK * CT, chunk_n(sc));
+      if (lane < CT) {
+        const float G = sc[SC_G * CT + lane], lr = __builtin_amdgcn_logf(sc[SC_RK * CT + lane]);
+        sc[SC_LA * CT + lane] = G + (__builtin_amdgcn_logf(sc[SC_BETA * CT + lane]) + lr);
+        sc[SC_LK0 * CT + lane] = G - lr;
+      }
+      acc = rows_mm(sK, sK);
+    } else {
+      if (lane < CT) {
+        const float G = sc[SC_G * CT + lane], lr = __builtin_amdgcn_logf(sc[SC_RK * CT + lane]);
+        sc[SC_LA * CT + lane] = G + (__builtin_amdgcn_logf(sc[SC_BETA * CT + lane]) + lr);
+        sc[SC_LK0 * CT + lane] = G - lr;
+      }
+      acc = rows_mm(sK, sK);
+    }
+    const float lki = sc[SC_LK0 * CT + c];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int tb = 8 * q4 + 4 * g;
+      const float4 L4 = *reinterpret_cast<const float4*>(sc + SC_LA * CT + tb);
+      const float La[4] = {L4.x, L4.y, L4.z, L4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tb + r;
+        const float f = exp2f_hw(La[r] - lki) * acc[4 * q4 + r];
+        sA[c * LDA + (t % LPC) * MPL + MPL - 1 - t / LPC] = c < t ? f : 0.f;
+      }
+    }
+    if (lane < CT) {
+      const float G = sc[SC_G * CT + lane], GC = sc[SC_G * CT + CT - 1];
+      const float rk = sc[SC_RK * CT + lane];
+      sc[SC_CK * CT + lane] = rk * exp2f_hw(G);
+      if constexpr (!CONV) sc[SC_CQ * CT + lane] = a.scale * sc[SC_RQ * CT + lane] * exp2f_hw(G);
+      sc[SC_CU * CT + lane] = rk * exp2f_hw(GC - G);
+    }
+  };
+  // the q tile of chunk cq to fp16 (CONV) and its output factor
+  auto convert_q = [&](int cq) {
+    float* sc = ringSc(cq);
+    convert_tile(ringQ(cq), sc + SC_RQ * CT, chunk_n(sc));
+    if (lane < CT) sc[SC_CQ * CT + lane] = a.scale * sc[SC_RQ * CT + lane] * exp2f_hw(sc[SC_G * CT + lane]);
+  };
+  // P[t][i] = scale r_q,t r_k,i e^{G_t - G_i} q_t.k_i (i <= t) of chunk cp, row t fp16
+  auto kq = [&](int cp) {
+    float* sc = ringSc(cp);
+    uint16_t* sP = ringP(cp);
+    if (lane < CT) {
+      const float G = sc[SC_G * CT + lane];
+      sc[SC_LQ * CT + lane] = G + __builtin_amdgcn_logf(sc[SC_RQ * CT + lane]);
+      sc[SC_LK1 * CT + lane] = G - __builtin_amdgcn_logf(sc[SC_RK * CT + lane]);
+    }
+    const f32x16 acc = rows_mm(ringK(cp), ringQ(cp));
+    const float lqt = sc[SC_LQ * CT + c];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int ib = 8 * q4 + 4 * g;
+      const float4 L4 = *reinterpret_cast<const float4*>(sc + SC_LK1 * CT + ib);
+      const float Lk[4] = {L4.x, L4.y, L4.z, L4.w};
+      float pv4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = a.scale * exp2f_hw(lqt - Lk[r]) * acc[4 * q4 + r];
+        pv4[r] = ib + r <= c ? f : 0.f;
+      }
+      *reinterpret_cast<u32x2*>(sP + c * LDT + ib) =
+          u32x2{pack_f16(pv4[0], pv4[1]), pack_f16(pv4[2], pv4[3])};
+    }
+  };
+
+  // the factor waves' part of interval it: the Gram tile of chunk it - 1
+  // (wave NSW + NLW), the K Q^T tile of chunk it - 1 (the next wave; with
+  // CONV it converts the q tile of chunk it - 1 and forms the K Q^T tile of
+  // chunk it - 2), the substitution of chunk it - 2 (the other two)
   auto factor = [&](int it) {
     const int fw = wave - NSW - C::NLW, ftid = tid - C::F0;
     const int cg = it - 1;
-    if (cg >= 0 && cg < nch) {
-      const uint16_t* sK = ringK(cg);
-      float* sc = ringSc(cg);
-      if (fw == 0) {
-        // A[t][i] = beta_t r_t r_i e^{G_t - G_i} k_t.k_i (i < t), stored
-        // transposed with rows interleaved over the substitution's lane parts
-        float* sA = bufA(cg);
-        if (lane < CT) {
-          const float G = sc[SC_G * CT + lane], lr = __builtin_amdgcn_logf(sc[SC_RK * CT + lane]);
-          sc[SC_LA * CT + lane] = G + (__builtin_amdgcn_logf(sc[SC_BETA * CT + lane]) + lr);
-          sc[SC_LK0 * CT + lane] = G - lr;
-        }
-        const f32x16 acc = rows_mm(sK, sK);
-        const float lki = sc[SC_LK0 * CT + c];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int tb = 8 * q4 + 4 * g;
-          const float4 L4 = *reinterpret_cast<const float4*>(sc + SC_LA * CT + tb);
-          const float La[4] = {L4.x, L4.y, L4.z, L4.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = tb + r;
-            const float f = exp2f_hw(La[r] - lki) * acc[4 * q4 + r];
-            sA[c * LDA + (t % LPC) * MPL + MPL - 1 - t / LPC] = c < t ? f : 0.f;
-          }
-        }
-        if (lane < CT) {
-          const float G = sc[SC_G * CT + lane], GC = sc[SC_G * CT + CT - 1];
-          const float rk = sc[SC_RK * CT + lane];
-          sc[SC_CK * CT + lane] = rk * exp2f_hw(G);
-          sc[SC_CQ * CT + lane] = a.scale * sc[SC_RQ * CT + lane] * exp2f_hw(G);
-          sc[SC_CU * CT + lane] = rk * exp2f_hw(GC - G);
-        }
-      } else if (fw == 1) {
-        // P[t][i] = scale r_q,t r_k,i e^{G_t - G_i} q_t.k_i (i <= t), row t fp16
-        uint16_t* sP = ringP(cg);
-        if (lane < CT) {
-          const float G = sc[SC_G * CT + lane];
-          sc[SC_LQ * CT + lane] = G + __builtin_amdgcn_logf(sc[SC_RQ * CT + lane]);
-          sc[SC_LK1 * CT + lane] = G - __builtin_amdgcn_logf(sc[SC_RK * CT + lane]);
-        }
-        const f32x16 acc = rows_mm(sK, ringQ(cg));
-        const float lqt = sc[SC_LQ * CT + c];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int ib = 8 * q4 + 4 * g;
-          const float4 L4 = *reinterpret_cast<const float4*>(sc + SC_LK1 * CT + ib);
-          const float Lk[4] = {L4.x, L4.y, L4.z, L4.w};
-          float pv4[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float f = a.scale * exp2f_hw(lqt - Lk[r]) * acc[4 * q4 + r];
-            pv4[r] = ib + r <= c ? f : 0.f;
-          }
-          *reinterpret_cast<u32x2*>(sP + c * LDT + ib) =
-              u32x2{pack_f16(pv4[0], pv4[1]), pack_f16(pv4[2], pv4[3])};
-        }
+    if (fw == 0) {
+      if (cg >= 0 && cg < nch) gram(cg);
+    } else if (fw == 1) {
+      if constexpr (CONV) {
+        if (cg >= 0 && cg < nch) convert_q(cg);
+        if (cg >= 1 && cg - 1 < nch) kq(cg - 1);
+      } else {
+        if (cg >= 0 && cg < nch) kq(cg);
       }
     }
 
@@ -601,17 +815,30 @@ pipelined_prefill_kernel(const ScanArgs a) {
       __syncthreads();
     }
   } else if (nch > 0) {
-    Rows R0, R1;
-    fetch(R0);
-    __builtin_amdgcn_sched_barrier(0);   // chunk 0's loads first: the first staging waits for them alone
-    fetch(R1);
-    for (int it = 0; it < nint; it += 2) {   // two intervals per trip: R0 even, R1 odd
-      load_stage(R0, it);
-      __syncthreads();
-      load_stage(R1, it + 1);
-      __syncthreads();
+    if constexpr (CONV) {
+      RowsX R;
+      first_x(R);
+      for (int it = 0; it < nint; ++it) {
+        load_stage_x(R, it);
+        __syncthreads();
+      }
+    } else {
+      Rows R0, R1;
+      fetch(R0);
+      __builtin_amdgcn_sched_barrier(0);   // chunk 0's loads first: the first staging waits for them alone
+      fetch(R1);
+      for (int it = 0; it < nint; it += 2) {   // two intervals per trip: R0 even, R1 odd
+        load_stage(R0, it);
+        __syncthreads();
+        load_stage(R1, it + 1);
+        __syncthreads();
+      }
     }
   } else {
+    // an empty prompt: its conv state passes through
+    if constexpr (CONV)
+      if (lw < 3 && own_win && a.conv_state_own)
+        write_window(static_cast<uint16_t*>(a.conv_state_out) + (size_t)s * 3 * a.conv_dim);
     for (int it = 0; it < nint; ++it) __syncthreads();
   }
   if (wave < NSW && a.final_state)

@@ -199,6 +199,44 @@ GDN_API gdn_status gdn_prefill_packed(const gdn_shape* shape, const int32_t* cu_
                               int32_t n_ckpt, void* out, float* final_state, float* ckpt_buf,
                               void* stream);
 
+/* Packed prefill with the short convolution fused into the scan's loads:
+ * the scan reads the pre-conv rows x and applies the width-4 causal conv +
+ * SiLU to q, k and v itself, so the conv output never goes through HBM (the
+ * in_proj -> GDN path is bandwidth-bound: vllm.cpp docs, "vLLM, online
+ * serving", ModelOpt table, the "Lever 2, GDN fp8 in_proj" row).  Results
+ * equal gdn_conv1d_silu_packed (x -> y, with the same conv states,
+ * checkpoints and windows) followed by gdn_prefill_packed on the column
+ * views q = y[:, :Hqk*dk], k = y[:, Hqk*dk:2*Hqk*dk], v = y[:, 2*Hqk*dk:],
+ * bit for bit: the conv runs in conv1d_silu's operation order and its bf16
+ * outputs are converted for the products exactly as loaded ones are.
+ *   shape:           bf16 io, dk = dv = 128, chunk 32 or 64 (the scan's
+ *                    32-token tiles); other shapes: GDN_ERR_UNSUPPORTED.
+ *                    q/k/v_tok_stride are not used.
+ *   x:               device bf16 [n_tokens, conv_dim], conv_dim = 2*Hqk*dk +
+ *                    Hv*dv, channels [q | k | v], token stride x_tok_stride
+ *                    in elements (0 = conv_dim).
+ *   conv_weight:     device fp32 [conv_dim, 4], tap 3 on the current token.
+ *   conv_state_in:   device bf16 [n_seqs, 3, conv_dim] (oldest first) or
+ *                    NULL (zeros).
+ *   conv_state_out:  device bf16 [n_seqs, 3, conv_dim] or NULL: each
+ *                    prompt's last three inputs.  May equal conv_state_in
+ *                    (the windows are then written by a second launch after
+ *                    the scan); must not overlap it otherwise.
+ *   conv_ckpt:       device bf16 [n_ckpt, 3, conv_dim] or NULL: the three
+ *                    inputs before each checkpoint.
+ *   the rest:        as gdn_prefill_packed.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE (also when out overlaps x),
+ * GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS, GDN_ERR_CKPT, GDN_ERR_HIP. */
+GDN_API gdn_status gdn_prefill_conv_packed(const gdn_shape* shape, const int32_t* cu_seqlens,
+                                   const int32_t* cu_seqlens_host, int32_t n_seqs,
+                                   int32_t n_tokens, const void* x, int64_t x_tok_stride,
+                                   const float* conv_weight, const void* conv_state_in,
+                                   void* conv_state_out, const float* g, const float* beta,
+                                   const float* init_state, const int32_t* ckpt_positions,
+                                   const int32_t* ckpt_positions_host, int32_t n_ckpt,
+                                   void* conv_ckpt, void* out, float* final_state,
+                                   float* ckpt_buf, void* stream);
+
 /* One recurrent step for each of `batch` decoding sequences, in place on a
  * state pool (one forward pass carries decodes beside a packed prefill:
  * sparkinfer release v0.6.4, "What changed"; packed GDN decode: vllm.cpp

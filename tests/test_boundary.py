@@ -188,6 +188,39 @@ def test_snapshot_and_conv_validation_errors():
                                       FAKE * 64, 0, None, None, None, 0, None, None) == 4
 
 
+@no_gpu
+def test_fused_conv_prefill_validation_errors():
+    lib = gdn.load()
+    cu = np.array([0, 40, 64], np.int32)
+    C = 2 * 2 * 128 + 4 * 128          # conv_dim at Hqk 2, Hv 4, d 128
+    def call(sh=None, cu=cu, T=64, x=FAKE, w=FAKE, out=1 << 32, ck=(), ckbuf=True, xs=0, st_in=None,
+             st_out=None):
+        sh = sh if sh is not None else gdn.make_shape(2, 4, 128, 128, 64)
+        ck = np.asarray(ck, np.int32)
+        return lib.gdn_prefill_conv_packed(
+            ctypes.byref(sh), FAKE, cu.ctypes.data, len(cu) - 1, T, x, xs, w, st_in, st_out, FAKE, FAKE,
+            None, FAKE if len(ck) else None, ck.ctypes.data if len(ck) else None, len(ck), None, out,
+            None, FAKE if (ckbuf and len(ck)) else None, None)
+    # only the fused kernel's shape: bf16, d_k = d_v = 128, 32-token tiles
+    assert call(gdn.make_shape(2, 4, 64, 64, 64)) == 3
+    assert call(gdn.make_shape(2, 4, 128, 64, 64)) == 3
+    assert call(gdn.make_shape(2, 4, 128, 128, 16)) == 3
+    assert call(gdn.make_shape(2, 4, 128, 128, 64, gdn.GDN_F32)) == 3
+    assert call(gdn.make_shape(2, 3, 128, 128, 64)) == 3
+    assert call(x=None) == 1
+    assert call(w=None) == 1
+    assert call(out=None) == 1
+    assert call(cu=np.array([0, 40, 63], np.int32)) == 4
+    assert call(ck=(40, 40)) == 5
+    assert call(ck=(16,), ckbuf=False) == 1
+    assert call(xs=C - 8) == 2                      # shorter than a row
+    assert call(xs=C + 4) == 2                      # rows not 16-byte aligned
+    assert call(x=FAKE + 8) == 2                    # misaligned
+    assert call(st_in=FAKE + 4) == 2
+    assert call(out=FAKE + 64 * C) == 2             # out overlapping x's last row
+    assert call(cu=np.array([0], np.int32), T=0) == 0   # an empty pack: nothing to do
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(gdn, "_lib", None)
     monkeypatch.setattr(gdn, "LIB_PATH", "/nonexistent/libgdn.so")
