@@ -329,6 +329,63 @@ def bench_layer_step(torch, gdn, p, steps, warmup, stream, label, fused=False):
     }
 
 
+def bench_conv_fused_packs(torch, gdn, stream, flush, reps, W):
+    """Scan and conv per pack: the conv kernel, the scan on its output, both
+    in turn, and the scan with the conv fused into its loads (one call, the
+    same conv states and windows), for the chat wave, the long prompts and
+    the ragged pack (each with its conv inputs)."""
+    packs = {"chat": W.chat_wave(seed=0, with_conv=True),
+             "long": W.make_pack("long_4x8192_conv", [8192] * 4, 16, 32, 128, 128, 64, 1024,
+                                 with_conv=True, conv_std=0.5),
+             "ragged": W.make_pack("ragged_8_conv", W._ragged_lengths(), 16, 32, 128, 128, 64, 256,
+                                   with_conv=True, conv_std=0.5, init_std=0.1)}
+    res = {}
+    for name, p in packs.items():
+        T, N, C = p.n_tokens, p.n_seqs, 2 * p.Hqk * p.dk + p.Hv * p.dv
+        ck = gdn.gdn_plan_checkpoints(p.cu_seqlens, p.block)
+        n_ck = len(ck)
+        x, w = io_t(torch, p.x, "bf16"), f32_t(torch, p.conv_w)
+        y = torch.empty_like(x)
+        st = torch.empty((N, 3, C), dtype=torch.bfloat16, device="cuda:0")
+        cck = torch.empty((max(n_ck, 1), 3, C), dtype=torch.bfloat16, device="cuda:0")
+        cu, ckd = i32_t(torch, p.cu_seqlens), i32_t(torch, ck)
+        g, beta = f32_t(torch, p.g), f32_t(torch, p.beta)
+        init = None if p.init is None else f32_t(torch, p.init)
+        out = torch.empty((T, p.Hv, p.dv), dtype=torch.bfloat16, device="cuda:0")
+        fin = torch.empty((N, p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
+        ckb = torch.empty((max(n_ck, 1), p.Hv, p.dv, p.dk), dtype=torch.float32, device="cuda:0")
+        sh = gdn.make_shape(p.Hqk, p.Hv, p.dk, p.dv, p.chunk, q_tok_stride=C, k_tok_stride=C,
+                            v_tok_stride=C)
+        Hd = p.Hqk * p.dk
+
+        def conv():
+            gdn.gdn_conv1d_silu_packed(sh, cu, p.cu_seqlens, x, w, y, None, st, ckd, ck, cck, stream=stream)
+
+        def scan():
+            gdn.gdn_prefill_packed(sh, cu, p.cu_seqlens, y[:, :Hd], y[:, Hd:2 * Hd], y[:, 2 * Hd:], g, beta,
+                                   init, ckd, ck, out, fin, ckb, stream=stream)
+
+        def both():
+            conv()
+            scan()
+
+        def fused():
+            gdn.gdn_prefill_conv_packed(sh, cu, p.cu_seqlens, x, w, g, beta, init, ckd, ck, out, fin, ckb,
+                                        conv_state_out=st, conv_ckpt=cck, stream=stream)
+        r = {"tokens": T, "prompts": N}
+        with torch.cuda.stream(stream):
+            for lab, fn in (("conv_ms", conv), ("scan_ms", scan), ("conv_then_scan_ms", both),
+                            ("fused_ms", fused)):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                r[lab] = statistics.median(Timer(torch, stream).run(fn, reps, flush))
+        r["fused_vs_two_launches"] = r["fused_ms"] / r["conv_then_scan_ms"]
+        res[name] = r
+        del x, y, out, fin, ckb
+    return res
+
+
 def bench_conv(torch, gdn, stream, flush, reps):
     T, Hqk, Hv, d = 32768, 16, 32, 128
     C = 2 * Hqk * d + Hv * d
@@ -704,6 +761,8 @@ def main():
                 "on its own stream", fused=True)
             legs["step_conv_fused"]["vs_two_launches"] = (legs["step_conv_fused"]["ms_per_step"] /
                                                           head["ms_median"])
+            log("[bench] leg conv_fused_packs")
+            legs["conv_fused_packs"] = bench_conv_fused_packs(torch, gdn, stream, flush, 10, W)
             log("[bench] leg scan_only")
             legs["scan_only"], _ = bench_prefill(torch, gdn, p, args.steps, args.warmup, stream, flush,
                                                  makers["chat"][1] + ", scan alone (dense q, k, v)")

@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(kThreads) conv_silu_kernel(const ConvArgs a, i
 #pragma unroll
   for (int c = 0; c < kVec; ++c) {
     const float4 t = reinterpret_cast<const float4*>(a.w)[c0 + c];
-    w[c][0] = t.x; w[c][1] = t.y; w[c][2] = t.z; w[c][3] = t.w;
+    w[c][0] = conv_tap(t.x); w[c][1] = conv_tap(t.y); w[c][2] = conv_tap(t.z); w[c][3] = conv_tap(t.w);
   }
   typedef const int32_t __attribute__((address_space(4)))* ConstI32;
   const ConstI32 cu = (ConstI32)a.cu;   // block-uniform reads: scalar loads

@@ -82,18 +82,22 @@ __device__ __forceinline__ void store16f(float* p, const float* v) {
 }
 
 // ------------------------------------------------------------- conv --
-// The width-4 causal depthwise conv + SiLU of one channel: w0..w3 the taps
-// (w3 on the current input), x0..x3 the inputs oldest first.  One operation
-// order everywhere it is computed, so every kernel gives the same bits.
-// silu(x) = x / (1 + e^-x) with the hardware exp and reciprocal (about 1 ulp
-// each, below the bf16 output rounding); large |x| saturates to x or -0.
+// The width-4 causal depthwise conv + SiLU of one channel, in one operation
+// order everywhere it is computed, so every kernel gives the same bits.  The
+// taps arrive scaled by -log2(e) (conv_tap; w3 on the current input), x0..x3
+// are the inputs oldest first.  With z' = -log2(e) z,
+//   silu(z) = z / (1 + e^-z) = z' / (-log2(e) (1 + 2^z')),
+// evaluated with the hardware exp2 and reciprocal (about 1 ulp each, below
+// the bf16 output rounding); large |z| saturates to z or -0.
+constexpr float kNegLog2e = -1.44269504088896341f;
+__device__ __forceinline__ float conv_tap(float w) { return w * kNegLog2e; }
 __device__ __forceinline__ float conv4_silu(float w0, float w1, float w2, float w3, float x0, float x1,
                                             float x2, float x3) {
-  float acc = w0 * x0;
-  acc = fmaf(w1, x1, acc);
-  acc = fmaf(w2, x2, acc);
-  acc = fmaf(w3, x3, acc);
-  return acc * __builtin_amdgcn_rcpf(1.0f + __expf(-acc));
+  float zs = w0 * x0;
+  zs = fmaf(w1, x1, zs);
+  zs = fmaf(w2, x2, zs);
+  zs = fmaf(w3, x3, zs);
+  return zs * __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(zs), kNegLog2e, kNegLog2e));
 }
 
 // fp32 -> bf16 -> fp32 (nearest even), the value a bf16 store would hold.

@@ -384,7 +384,8 @@ pipelined_prefill_kernel(const ScanArgs a) {
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const float4 w4 = reinterpret_cast<const float4*>(a.conv_w)[xch + c2];
-        cw[c2][0] = w4.x; cw[c2][1] = w4.y; cw[c2][2] = w4.z; cw[c2][3] = w4.w;
+        cw[c2][0] = conv_tap(w4.x); cw[c2][1] = conv_tap(w4.y);
+        cw[c2][2] = conv_tap(w4.z); cw[c2][3] = conv_tap(w4.w);
       }
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
@@ -420,11 +421,12 @@ pipelined_prefill_kernel(const ScanArgs a) {
     last_t0 = t0x;
     last_n = nx;
   };
-  // row min(t, nx - 1) of the chunk at t0x, the lane's two channels
+  // row min(t, nx - 1) of the chunk at t0x, the lane's two channels (a
+  // row base held in scalar registers, the lane's offset fixed)
   auto xrow = [&](int t0x, int t, int nx) {
-    const char* xb = static_cast<const char*>(a.conv_x) + (size_t)t0x * a.conv_x_stride * 2;
-    return *reinterpret_cast<const uint32_t*>(
-        row(xb, __umul24(min(t, nx - 1), (uint32_t)a.conv_x_stride * 2) + 2 * xch));
+    const char* rp = static_cast<const char*>(a.conv_x) +
+                     (size_t)(t0x + min(t, nx - 1)) * (size_t)a.conv_x_stride * 2;
+    return *reinterpret_cast<const uint32_t*>(rp + 2 * xch);
   };
   auto gates_x = [&](RowsX& R, int t0x, int nx) {
     const uint32_t tl = min(lane, nx - 1);
@@ -458,8 +460,9 @@ pipelined_prefill_kernel(const ScanArgs a) {
         uint32_t* dcol = reinterpret_cast<uint32_t*>(dst) + lane;
         const int ldw = (lw == 2 ? LDV : LDK) / 2;
         // row t of the chunk: conv + SiLU from the carried inputs, the next
-        // chunk's row t requested into the freed register
-        auto conv_row = [&](int t, bool valid) {
+        // chunk's row t requested into the freed register; the v wave also
+        // takes the rows' largest |v|
+        auto conv_row = [&](int t, bool valid, auto with_vm) {
           uint32_t o = 0;   // rows past n: zeros
           if (valid) {
             const float x0 = __uint_as_float(R.x[t] << 16), x1 = __uint_as_float(R.x[t] & 0xFFFF0000u);
@@ -472,19 +475,27 @@ pipelined_prefill_kernel(const ScanArgs a) {
           }
           R.x[t] = xrow(t0n, t, nn);
           dcol[t * ldw] = o;
-          vm = bf16_absmax(vm, o);   // used by the v wave
-          asm volatile("" : "+v"(vm));   // taken here: deferred, it keeps every row's output live
-        };
-        if (n == CT) {   // a whole chunk: no branches, the rows interleave
-#pragma unroll
-          for (int t = 0; t < CT; ++t) {
-            conv_row(t, true);
-            if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // four rows in flight
+          if constexpr (decltype(with_vm)::value) {
+            vm = bf16_absmax(vm, o);
+            asm volatile("" : "+v"(vm));   // taken here: deferred, it keeps every row's output live
           }
-        } else {
+        };
+        auto conv_rows = [&](auto with_vm) {
+          if (n == CT) {   // a whole chunk: no branches, the rows interleave
 #pragma unroll
-          for (int t = 0; t < CT; ++t) conv_row(t, t < n);
-        }
+            for (int t = 0; t < CT; ++t) {
+              conv_row(t, true, with_vm);
+              if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // four rows in flight
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < CT; ++t) conv_row(t, t < n, with_vm);
+          }
+        };
+        if (lw == 2)
+          conv_rows(std::true_type{});
+        else
+          conv_rows(std::false_type{});
         if (own_win) {
           if (R.ck >= 0 && a.conv_ckpt) write_window(static_cast<uint16_t*>(a.conv_ckpt) + (size_t)R.ck * 3 * a.conv_dim);
           if (cs == nch - 1 && a.conv_state_own)

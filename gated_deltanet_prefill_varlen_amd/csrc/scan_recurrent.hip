@@ -184,7 +184,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
                                   : cst + ((size_t)r * 3 + 3 + pp) * a.conv_dim + ch);
       }
       const float4 w = reinterpret_cast<const float4*>(a.conv_w)[ch];
-      const float y = conv4_silu(w.x, w.y, w.z, w.w, xw[0], xw[1], xw[2], xw[3]);
+      const float y = conv4_silu(conv_tap(w.x), conv_tap(w.y), conv_tap(w.z), conv_tap(w.w), xw[0], xw[1],
+                                 xw[2], xw[3]);
       conv_out[e] = IO::kBytes == 2 ? round_bf16(y) : y;
     }
     __syncthreads();

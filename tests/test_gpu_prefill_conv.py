@@ -133,10 +133,10 @@ def test_fused_equals_two_launches_ragged(Hqk, Hv):
     print(f"ragged fused: Hqk {Hqk} Hv {Hv} T {p.n_tokens} ckpts {len(ck)}", flush=True)
     c = Case(p, ck)
     ref = c.two_launches()
-    got = c.fused()
     torch.cuda.synchronize()
     assert not torch.equal(ref["out"], torch.full_like(ref["out"], 7.0))
-    assert_same(ref, got, "ragged")
+    for rep in range(3):   # every run the same bits
+        assert_same(ref, c.fused(), f"ragged, run {rep}")
 
 
 def test_fused_equals_two_launches_variants():
