@@ -97,6 +97,129 @@ def measured_traffic(workload: str):
     return None if w is None else float(w["hbm_bytes_per_launch"])
 
 
+# ------------------------------------------------- profile summaries (host) --
+
+PREFILL_GRIDS = {786432: "chat", 98304: "long", 196608: "ragged"}   # work-items: workgroups x 768
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(prof_dir: str) -> dict:
+    """Summaries of a rocprofv3 run set of this script: prof_dir/trace (kernel
+    trace with stats), prof_dir/FETCH_SIZE and prof_dir/WRITE_SIZE (one
+    counter each).  Prefill dispatches are told apart by grid size (chat wave,
+    long prompts, ragged pack) and by kernel variant (the conv fused or not);
+    the counters, in KiB per dispatch, are scaled by what they read for the
+    device-pool checkpoint copy of the same run (96 items of 2 MiB read and
+    written).  Writes profiles/traffic.json for the current kernel sources
+    and returns the tables."""
+    import collections
+    def pref(name):
+        if "pipelined_prefill_kernel<128, 128, false>" in name:
+            return ""
+        if "pipelined_prefill_kernel<128, 128, true>" in name:
+            return "conv_fused_"
+        return None
+    # kernel trace: durations per (kernel, grid)
+    tr = collections.defaultdict(list)
+    for r in _csv_rows(os.path.join(prof_dir, "trace"), "kernel_trace.csv"):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        tr[(r["Kernel_Name"], grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    stats = _csv_rows(os.path.join(prof_dir, "trace"), "kernel_stats.csv")
+    # counters
+    cnt = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        agg = collections.defaultdict(list)
+        for r in _csv_rows(os.path.join(prof_dir, c), "counter_collection.csv"):
+            agg[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        cnt[c] = {k: (len(v), sum(v) / len(v)) for k, v in agg.items()}
+    copies = [k for k in cnt["WRITE_SIZE"] if "snapshot_copy_kernel" in k[0]]
+    ck = max(copies, key=lambda k: k[1])              # the device pool: most workgroups
+    true_kib = 96 * 2 * 1024
+    ff = true_kib / cnt["FETCH_SIZE"][ck][1]
+    wf = true_kib / cnt["WRITE_SIZE"][ck][1]
+    work = {}
+    for (name, grid), (n, fk) in cnt["FETCH_SIZE"].items():
+        pf = pref(name)
+        if pf is None or grid not in PREFILL_GRIDS:
+            continue
+        wk = cnt["WRITE_SIZE"].get((name, grid), (0, float("nan")))[1]
+        durs = tr.get((name, grid), [])
+        work[pf + PREFILL_GRIDS[grid]] = {
+            "fetch_kib": fk, "write_kib": wk, "hbm_bytes_per_launch": (fk * ff + wk * wf) * 1024,
+            "dispatches": n, "trace_dispatches": len(durs),
+            "trace_avg_us": statistics.fmean(durs) if durs else None}
+    rec = {"csrc_sha256": csrc_digest(), "fetch_factor": ff, "write_factor": wf,
+           "copy_kib_true": float(true_kib), "copy_fetch_kib": cnt["FETCH_SIZE"][ck][1],
+           "copy_write_kib": cnt["WRITE_SIZE"][ck][1], "workloads": work}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    top = sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:10]
+    return {"traffic": rec, "kernel_stats_top": [
+        {"kernel": r["Name"], "calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+         "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
+         "percent": float(r["Percentage"])} for r in top]}
+
+
+def summarize_sq(prof_dir: str) -> dict:
+    """SQ counter summaries of the prefill kernel per workload, from
+    prof_dir/sq_<workload>_p<k> (several counter passes of `--no-legs
+    --workload <workload>` runs): medians over the workload's prefill
+    dispatches, per workgroup and chunk, and busy and wait fractions.  The
+    wave-cycle counters count 4-cycle units; GRBM_GUI_ACTIVE is summed over
+    the 8 XCDs."""
+    import collections
+    import glob
+    import workloads as W
+    packs = {"chat": W.chat_wave(seed=0), "long": W.long_prompts(seed=0), "ragged": W.ragged_pack(seed=0)}
+    out = {}
+    for w, p in packs.items():
+        grid = {"chat": 786432, "long": 98304, "ragged": 196608}[w]
+        vals = collections.defaultdict(list)
+        times = []
+        for d in sorted(x for x in glob.glob(os.path.join(prof_dir, f"sq_{w}_p*")) if os.path.isdir(x)):
+            for r in _csv_rows(d, "counter_collection.csv"):
+                if "pipelined_prefill_kernel<128, 128, false>" in r["Kernel_Name"] and int(r["Grid_Size"]) == grid:
+                    vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+                    if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                        times.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        if not vals:
+            continue
+        m = {k: statistics.median(v) for k, v in vals.items()}
+        wgs = p.n_seqs * p.Hv
+        lens = np.diff(p.cu_seqlens)
+        chunks = int(sum((int(L) + 31) // 32 for L in lens)) * p.Hv
+        cycles = m["GRBM_GUI_ACTIVE"] / 8
+        simds = 1024
+        used = min(wgs, 256) * 4
+        t_us = statistics.median(times)
+        per = {k: m[k] / chunks for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+                                          "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR") if k in m}
+        out[w] = {
+            "workgroups": wgs, "chunks": chunks, "dispatches": len(times), "dispatch_us": t_us,
+            "clock_GHz": cycles / t_us / 1e3,
+            "per_workgroup_chunk": per,
+            "cycles_per_chunk_interval": cycles / (chunks / min(wgs, 256)) if wgs else None,
+            "valu_busy_all_simds": 4 * m["SQ_ACTIVE_INST_VALU"] / (simds * cycles),
+            "valu_busy_used_simds": 4 * m["SQ_ACTIVE_INST_VALU"] / (used * cycles),
+            "mfma_busy_used_simds": m["SQ_VALU_MFMA_BUSY_CYCLES"] / (used * cycles),
+            "waves_per_simd_all": 4 * m["SQ_WAVE_CYCLES"] / (simds * cycles),
+            "waves_per_simd_used": 4 * m["SQ_WAVE_CYCLES"] / (used * cycles),
+            "wait_any_frac": m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"],
+            "wait_lds_frac": m["SQ_WAIT_INST_LDS"] / m["SQ_WAVE_CYCLES"],
+            "lds_bank_conflict_frac": m["SQ_LDS_BANK_CONFLICT"] / m["SQ_LDS_IDX_ACTIVE"],
+            "raw_medians": m}
+    return out
+
+
 # --------------------------------------------------------------- GPU legs --
 
 class Timer:
@@ -696,9 +819,18 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-prompts", type=int, default=32)
     ap.add_argument("--workload", default="chat", choices=["chat", "long", "ragged"])
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="summarize a rocprofv3 run set of this script (no GPU) and exit")
     ap.add_argument("--overlap-only", action="store_true",
                     help="run only the stream-overlap leg (for a rocprofv3 timeline)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        d = args.summarize_profiles
+        res = summarize_profiles(d) if os.path.isdir(os.path.join(d, "FETCH_SIZE")) else {}
+        if any(n.startswith("sq_") for n in os.listdir(d)):
+            res["sq"] = summarize_sq(d)
+        print(json.dumps(res, indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: one GPU only (the path would shard by value-head groups with no exchange "
               "between GPUs; multi-GPU runs are not implemented). Use --gpus 1.", file=sys.stderr)
