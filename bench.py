@@ -169,6 +169,47 @@ def summarize_profiles(prof_dir: str) -> dict:
          "percent": float(r["Percentage"])} for r in top]}
 
 
+def summarize_overlap(trace_dir: str) -> dict:
+    """Kernels of the path on different hardware queues whose [start, end)
+    intervals intersect, from a kernel trace of `--overlap-only`: per pair of
+    (kernel, grid work-items), the count, the summed overlap and the summed
+    duration of the shorter kernel; plus the mixed pass's steady-state loop
+    (prefill pack and decode batch dispatches in it: start gap and span)."""
+    import collections
+    rows = _csv_rows(trace_dir, "kernel_trace.csv")
+    ev = []
+    for r in rows:
+        n = r["Kernel_Name"]
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        kind = ("prefill" if "pipelined_prefill_kernel" in n else "decode" if "decode_kernel" in n
+                else "copy" if "snapshot_copy_kernel" in n else None)
+        if kind:
+            ev.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), f"{kind}({grid})", r["Queue_Id"]))
+    ev.sort()
+    pairs = collections.defaultdict(lambda: [0, 0.0, 0.0])
+    mixed = []
+    for i, a in enumerate(ev):
+        for b in ev[i + 1:]:
+            if b[0] >= a[1]:
+                break
+            if a[3] == b[3]:
+                continue
+            key = " + ".join(sorted((a[2], b[2])))
+            ov = (min(a[1], b[1]) - b[0]) / 1e3
+            pairs[key][0] += 1
+            pairs[key][1] += ov
+            pairs[key][2] += min(a[1] - a[0], b[1] - b[0]) / 1e3
+            if {a[2].split("(")[0], b[2].split("(")[0]} == {"prefill", "decode"}:
+                mixed.append({"gap_us": (b[0] - a[0]) / 1e3, "span_us": (max(a[1], b[1]) - a[0]) / 1e3,
+                              "first_us": (a[1] - a[0]) / 1e3, "second_us": (b[1] - b[0]) / 1e3,
+                              "first": a[2]})
+    med = lambda k: statistics.median(m[k] for m in mixed) if mixed else None
+    return {"pairs": {k: {"count": v[0], "overlap_us": v[1], "shorter_us": v[2],
+                          "share": v[1] / v[2] if v[2] else None} for k, v in pairs.items()},
+            "mixed_pass_pairs": len(mixed),
+            "mixed_pass_median": {k: med(k) for k in ("gap_us", "span_us", "first_us", "second_us")}}
+
+
 def summarize_sq(prof_dir: str) -> dict:
     """SQ counter summaries of the prefill kernel per workload, from
     prof_dir/sq_<workload>_p<k> (several counter passes of `--no-legs
@@ -724,6 +765,61 @@ def bench_overlap(torch, gdn, stream, flush, reps):
     t_two = med(joined(pre, dec_b), sA)
     out["mixed_pass"] = {"prefill_ms": t_p, "decode_ms": t_d, "one_stream_ms": t_serial,
                          "two_streams_ms": t_two, "overlap_saved_ms": t_serial - t_two}
+    # K passes back to back as a serving loop issues them (one cache flush
+    # ahead of the region, none between passes): one stream; two streams
+    # joined after every pass (the next pass starts when both parts ended);
+    # two streams each running its part of every pass, joined once at the end
+    K = 50
+
+    def region(body):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sA):
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(sA)
+        body()
+        b.record(sA)
+        b.synchronize()
+        return a.elapsed_time(b) / K
+
+    def fork():
+        e = torch.cuda.Event()
+        e.record(sA)
+        sB.wait_event(e)
+
+    def join():
+        e = torch.cuda.Event()
+        e.record(sB)
+        sA.wait_event(e)
+
+    def loop_one():
+        for _ in range(K):
+            pre()
+            dec_a()
+
+    def loop_joined_each():
+        for _ in range(K):
+            fork()
+            pre()
+            dec_b()
+            join()
+
+    def loop_joined_once():
+        fork()
+        for _ in range(K):
+            pre()
+            dec_b()
+        join()
+    steady = {}
+    for name, body in (("prefill_only_ms", lambda: [pre() for _ in range(K)]),
+                       ("decode_only_ms", lambda: [dec_a() for _ in range(K)]),
+                       ("one_stream_ms", loop_one), ("two_streams_joined_each_pass_ms", loop_joined_each),
+                       ("two_streams_joined_once_ms", loop_joined_once)):
+        region(body)
+        steady[name] = statistics.median(region(body) for _ in range(3))
+    steady["saved_joined_each_pass"] = 1 - steady["two_streams_joined_each_pass_ms"] / steady["one_stream_ms"]
+    steady["saved_joined_once"] = 1 - steady["two_streams_joined_once_ms"] / steady["one_stream_ms"]
+    out["mixed_pass"]["steady_state_per_pass"] = steady
     del dp
     # (b) checkpoint copy beside the next layer's scan
     p = W.chat_wave(seed=0)
@@ -829,6 +925,8 @@ def main():
         res = summarize_profiles(d) if os.path.isdir(os.path.join(d, "FETCH_SIZE")) else {}
         if any(n.startswith("sq_") for n in os.listdir(d)):
             res["sq"] = summarize_sq(d)
+        if os.path.isdir(os.path.join(d, "overlap")):
+            res["overlap"] = summarize_overlap(os.path.join(d, "overlap"))
         print(json.dumps(res, indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
