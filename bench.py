@@ -70,11 +70,19 @@ def step_min_bytes(p, n_ckpt: int) -> int:
     return prefill_alg_bytes(p, n_ckpt, p.init is not None) + C * 4 * 4 + p.n_seqs * 3 * C * 2
 
 
+# The C entry points' host-side validation: no device or launch code.
+HOST_ONLY_SOURCES = ("gdn_api.hip",)
+
+
 def csrc_digest() -> str:
-    """sha256 over the kernel sources (names and bytes, sorted by name)."""
+    """sha256 over the device and launch sources (names and bytes, sorted by
+    name): every file of csrc/ except the host-only validation of the entry
+    points, which changes no kernel and no launch."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
+        if name in HOST_ONLY_SOURCES:
+            continue
         h.update(name.encode())
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())

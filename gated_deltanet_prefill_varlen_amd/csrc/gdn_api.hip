@@ -2,6 +2,7 @@
 // and kernel dispatch.  No HIP call is made before a call is fully validated.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -67,6 +68,17 @@ gdn_status check_ckpts(const int32_t* cu, int32_t n_seqs, const int32_t* pos, in
     while (s < n_seqs && !(cu[s] < p && p <= cu[s + 1])) ++s;
     if (s >= n_seqs) return GDN_ERR_CKPT;
   }
+  return GDN_OK;
+}
+
+// Every slot in [0, pool_slots) and no slot twice; the check sorts a copy
+// of the n slots, so its host memory is O(n) whatever the pool's size.
+template <typename T>
+gdn_status check_slots(const T* slots, int64_t n, int64_t pool_slots) {
+  std::vector<int64_t> v(slots, slots + n);
+  std::sort(v.begin(), v.end());
+  for (int64_t i = 0; i < n; ++i)
+    if (v[i] < 0 || v[i] >= pool_slots || (i > 0 && v[i] == v[i - 1])) return GDN_ERR_CAPACITY;
   return GDN_OK;
 }
 
@@ -263,12 +275,7 @@ gdn_status gdn_decode_tokens(const gdn_shape* shape, int32_t batch, int32_t n_to
   if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_NULL;
   if (slot) {
     if (!slot_host) return GDN_ERR_NULL;
-    std::vector<char> seen((size_t)pool_slots, 0);
-    for (int32_t b = 0; b < batch; ++b) {
-      const int64_t r = slot_host[b];
-      if (r < 0 || r >= pool_slots || seen[(size_t)r]) return GDN_ERR_CAPACITY;
-      seen[(size_t)r] = 1;
-    }
+    if ((st = check_slots(slot_host, batch, pool_slots)) != GDN_OK) return st;
   } else if (batch > pool_slots) {
     return GDN_ERR_CAPACITY;
   }
@@ -355,12 +362,8 @@ gdn_status gdn_snapshot_copy(const void* ckpt_buf, int32_t n, int64_t bytes_each
     if (!ckpt_buf || !dst_pool || !dst_slot || !dst_slot_host) return GDN_ERR_NULL;
     if (bytes_each <= 0 || bytes_each % 16 != 0) return GDN_ERR_SHAPE;
     if (!aligned16(ckpt_buf) || !aligned16(dst_pool)) return GDN_ERR_SHAPE;
-    std::vector<char> seen((size_t)pool_slots, 0);
-    for (int32_t i = 0; i < n; ++i) {
-      const int64_t r = dst_slot_host[i];
-      if (r < 0 || r >= pool_slots || seen[(size_t)r]) return GDN_ERR_CAPACITY;
-      seen[(size_t)r] = 1;
-    }
+    const gdn_status sc = check_slots(dst_slot_host, n, pool_slots);
+    if (sc != GDN_OK) return sc;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(copy_stream);
   hipError_t e = hipSuccess;

@@ -156,6 +156,7 @@ def test_decode_validation_errors():
     assert call(slot=[0, 1, 1]) == 6
     assert call(slot=[0, 1, 5]) == 6
     assert call(slot=[0, -1, 2]) == 6
+    assert call(pool=1 << 40, slot=[0, 7, 7]) == 6   # a huge pool: the check is O(batch) on the host
     assert call(cw=FAKE) == 1                       # conv weights without conv states
     assert call(cs=FAKE) == 1                       # and the other way round
     assert call(cw=FAKE, cs=FAKE + 4) == 2          # misaligned conv state
@@ -178,6 +179,8 @@ def test_snapshot_and_conv_validation_errors():
     assert lib.gdn_snapshot_copy(FAKE, 3, 60, FAKE, 4, FAKE, sl.ctypes.data, None, None, None) == 2
     assert lib.gdn_snapshot_copy(FAKE, 3, 64, None, 4, FAKE, sl.ctypes.data, None, None, None) == 1
     assert lib.gdn_snapshot_copy(FAKE, 0, 64, None, 4, None, None, None, None, None) == 0
+    sl = np.array([5, 5], np.int64)   # a huge pool: the slot check needs no pool-sized memory
+    assert lib.gdn_snapshot_copy(FAKE, 2, 64, FAKE, 1 << 40, FAKE, sl.ctypes.data, None, None, None) == 6
     sh = gdn.make_shape(2, 2, 32, 32, 16, gdn.GDN_F32)
     cu = np.array([0, 40, 64], np.int32)
     # y overlapping x
