@@ -165,28 +165,31 @@ pipelined_prefill_kernel(const ScanArgs a) {
     }
   };
 
-  // The scale of the chunk whose scalars are at sc: from the chunk's largest
-  // |v| (recorded by the loader waves) and the largest |S| entry of the
-  // wave's columns (unscaled: 2^-E times the held value); the held state
-  // is rescaled when the scale changes (powers of two, exact).
-  auto choose_scale = [&](const float* sc) {
+  // The scale of a chunk, from the chunk's largest |v| (vmax: bf16 bits,
+  // recorded by the loader waves) and the largest |S| entry of the wave's
+  // columns (unscaled: 2^-E times the held value); the held state is
+  // rescaled when the scale changes (powers of two, exact).  Returns whether
+  // it changed.
+  auto chunk_vmax = [&](const float* sc) {
     const u32x4 vm4 = *reinterpret_cast<const u32x4*>(sc + SC_VM * CT);
-    __builtin_amdgcn_sched_barrier(0);   // the LDS read first: its latency under the |S| maximum
+    return __builtin_amdgcn_readfirstlane(max(max(vm4[0], vm4[1]), max(vm4[2], vm4[3])));
+  };
+  uint32_t vmax = 0;
+  auto rescale_if_needed = [&](uint32_t vmax) {
     float ms = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) ms = fmaxf(ms, fabsf(S[kt][i]));
     const int eS = f32_exp(__uint_as_float(wave_max_u32(__float_as_uint(ms))));
-    const int eV = bf16_exp(__builtin_amdgcn_readfirstlane(max(max(vm4[0], vm4[1]), max(vm4[2], vm4[3]))));
-    const int En = band_exp(max(eS == kNoExp ? kNoExp : eS - E, eV));
-    if (En != E) {   // rare
+    const int En = band_exp(max(eS == kNoExp ? kNoExp : eS - E, bf16_exp(vmax)));
+    if (En == E) return false;
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) S[kt][i] = __builtin_amdgcn_ldexpf(S[kt][i], En - E);
-      E = En;
-    }
+      for (int i = 0; i < 16; ++i) S[kt][i] = __builtin_amdgcn_ldexpf(S[kt][i], En - E);
+    E = En;
+    return true;
   };
 
   // One 16-dim piece pc of row t of a q or k tile (bf16 bits, two 8-value
@@ -709,25 +712,42 @@ pipelined_prefill_kernel(const ScanArgs a) {
         const float* sCk = sc + SC_CK * CT;
         const float* sCq = sc + SC_CQ * CT;
         const float* sCu = sc + SC_CU * CT;
-        if (cx == 0) choose_scale(sc);   // later chunks' scales: at the end of the chunk before
         // X = K S0^T and QS = S0 Q^T for this wave's columns (S0 rounded to
-        // fp16 per k tile), then the chunk's decay on S
-        f32x16 X = {}, QS = {};
+        // fp16 per k tile), then the chunk's decay on S.  The products are
+        // formed with the scale of the chunk before, while the chunk's own
+        // scale is chosen beside them; when it differs (rare) the held state
+        // is rescaled and the products formed again, so every chunk runs at
+        // its own scale and the update's results are not waited for before
+        // the barrier.
+        f32x16 X, QS;
         {
-          f16x8 ka[NKS], qa[NKS];
+          if (cx == 0) vmax = chunk_vmax(sc);
+          auto products = [&]() {
+            f16x8 ka[NKS], qa[NKS];
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            ka[ks] = lds_op(sK + c * LDK + 4 * g + 16 * ks);
-            qa[ks] = lds_op(sQ + c * LDK + 4 * g + 16 * ks);
-          }
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const f16x8 sh = h2 == 0 ? acc_half<0>(S[kt]) : acc_half<1>(S[kt]);
-              X = mma(ka[2 * kt + h2], sh, X);
-              QS = mma(sh, qa[2 * kt + h2], QS);
+            for (int ks = 0; ks < NKS; ++ks) {
+              ka[ks] = lds_op(sK + c * LDK + 4 * g + 16 * ks);
+              qa[ks] = lds_op(sQ + c * LDK + 4 * g + 16 * ks);
             }
+            X = f32x16{};
+            QS = f32x16{};
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+                const f16x8 sh = h2 == 0 ? acc_half<0>(S[kt]) : acc_half<1>(S[kt]);
+                X = mma(ka[2 * kt + h2], sh, X);
+                QS = mma(sh, qa[2 * kt + h2], QS);
+              }
+          };
+          products();
+          __builtin_amdgcn_sched_barrier(0);
+          if (__builtin_expect(rescale_if_needed(vmax), 0)) {   // rare: the scale changed
+            __builtin_amdgcn_sched_barrier(0);
+            products();
+          }
+          // the next chunk's largest |v|, staged two intervals ago
+          if (cx + 1 < nch) vmax = chunk_vmax(ringSc(cx + 1));
           const float gC = exp2f_hw(sc[SC_G * CT + CT - 1]);
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
@@ -814,9 +834,6 @@ pipelined_prefill_kernel(const ScanArgs a) {
                 u32x2{pack_bf16(QS[4 * q4], QS[4 * q4 + 1]), pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3])};
         }
         if (ck_at >= 0) store_state(a.ckpt_buf + (size_t)ck_at * sstride + ((size_t)h * DV + v) * DK);
-        // the next chunk's scale, here where the state waves would otherwise
-        // wait at the barrier (that chunk's scalars were staged two intervals ago)
-        if (cx + 1 < nch) choose_scale(ringSc(cx + 1));
       }
       __syncthreads();
     }
