@@ -804,9 +804,12 @@ pipelined_prefill_kernel(const ScanArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) QS[i] *= cq;
         }
-        // U's operand halves for the output product, which runs after the
-        // state update (off the recurrence; measured 1-5% faster)
+        // O^T = scale r_q e^G (S0 Q^T) + U^T P^T, token t = c per lane: its
+        // two products go ahead of the update's eight, so the output rows
+        // are stored while the update is still in the matrix pipe
         const f16x8 uo[2] = {acc_half<0>(U), acc_half<1>(U)};
+        QS = mma(uo[0], pA[0], QS);
+        QS = mma(uo[1], pA[1], QS);
         // S = (e^{G_C} S0) + K^T (r_k e^{G_C - G} U)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -819,10 +822,8 @@ pipelined_prefill_kernel(const ScanArgs a) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) S[kt] = mma(kta[2 * kt + h2], uh[h2], S[kt]);
-        // O^T = scale r_q e^G (S0 Q^T) + U^T P^T, token t = c per lane: the
-        // wave's 32 columns of row t go to HBM as four 8-byte bf16 pieces
-        QS = mma(uo[0], pA[0], QS);
-        QS = mma(uo[1], pA[1], QS);
+        // the wave's 32 columns of output row t go to HBM as four 8-byte
+        // bf16 pieces
         if (E != 0)
 #pragma unroll
           for (int i = 0; i < 16; ++i) QS[i] = __builtin_amdgcn_ldexpf(QS[i], -E);
