@@ -720,6 +720,7 @@ pipelined_prefill_kernel(const ScanArgs a) {
         // its own scale and the update's results are not waited for before
         // the barrier.
         f32x16 X, QS;
+        u32x2 vw[4];
         {
           if (cx == 0) vmax = chunk_vmax(sc);
           auto products = [&]() {
@@ -741,6 +742,10 @@ pipelined_prefill_kernel(const ScanArgs a) {
               }
           };
           products();
+          // V of this wave's columns by transpose reads (raw bf16, before the
+          // scale is known), their latency under the scale choice
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) vw[q4] = lds_tr4(sV + vtr + 8 * q4 * LDV);
           __builtin_amdgcn_sched_barrier(0);
           if (__builtin_expect(rescale_if_needed(vmax), 0)) {   // rare: the scale changed
             __builtin_amdgcn_sched_barrier(0);
@@ -758,14 +763,14 @@ pipelined_prefill_kernel(const ScanArgs a) {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) asm volatile("" : "+v"(S[kt]));
         }
-        // V of this wave's columns by transpose reads, then the T and P row
-        // operands and the K^T operands of the update, requested ahead
+        // V to fp32 (scaled by 2^E), then the T and P row operands and the
+        // K^T operands of the update, requested ahead
         const uint16_t* tr = bufT(cx) + c * LDT + 4 * g;
         const uint16_t* pr = ringP(cx) + c * LDT + 4 * g;
         float vv[16];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const u32x2 w = lds_tr4(sV + vtr + 8 * q4 * LDV);
+          const u32x2 w = vw[q4];
           vv[4 * q4] = __uint_as_float(w.x << 16);
           vv[4 * q4 + 1] = __uint_as_float(w.x & 0xFFFF0000u);
           vv[4 * q4 + 2] = __uint_as_float(w.y << 16);
