@@ -827,17 +827,34 @@ pipelined_prefill_kernel(const ScanArgs a) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) S[kt] = mma(kta[2 * kt + h2], uh[h2], S[kt]);
-        // the wave's 32 columns of output row t go to HBM as four 8-byte
-        // bf16 pieces
+        // the wave's 32 columns of output row t (64 bytes) go to HBM in two
+        // stores: the lane pair of row t (lane halves g = 0, 1, 8-byte pieces
+        // at 16 q4 + 8 g) trade pieces so that each store writes 32
+        // contiguous bytes of the row
         if (E != 0)
 #pragma unroll
           for (int i = 0; i < 16; ++i) QS[i] = __builtin_amdgcn_ldexpf(QS[i], -E);
-        if (c < n) {
-          uint16_t* orow = og + (size_t)(t0 + c) * a.Hv * DV + 32 * wave + 4 * g;
+        {
+          uint32_t P[4][2];
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<u32x2*>(orow + 8 * q4) =
-                u32x2{pack_bf16(QS[4 * q4], QS[4 * q4 + 1]), pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3])};
+          for (int q4 = 0; q4 < 4; ++q4) {
+            P[q4][0] = pack_bf16(QS[4 * q4], QS[4 * q4 + 1]);
+            P[q4][1] = pack_bf16(QS[4 * q4 + 2], QS[4 * q4 + 3]);
+          }
+          // half g = 0 takes the other half's pieces q4 = 0, 2; half 1 takes q4 = 1, 3
+#pragma unroll
+          for (int pr2 = 0; pr2 < 4; pr2 += 2)
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              const auto r = __builtin_amdgcn_permlane32_swap(P[pr2][d], P[pr2 + 1][d], false, false);
+              P[pr2][d] = r[0];
+              P[pr2 + 1][d] = r[1];
+            }
+          if (c < n) {
+            uint16_t* orow = og + (size_t)(t0 + c) * a.Hv * DV + 32 * wave + 8 * g;
+            *reinterpret_cast<u32x4*>(orow) = u32x4{P[0][0], P[0][1], P[1][0], P[1][1]};
+            *reinterpret_cast<u32x4*>(orow + 16) = u32x4{P[2][0], P[2][1], P[3][0], P[3][1]};
+          }
         }
         if (ck_at >= 0) store_state(a.ckpt_buf + (size_t)ck_at * sstride + ((size_t)h * DV + v) * DK);
       }
