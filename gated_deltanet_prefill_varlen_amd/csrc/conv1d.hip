@@ -1,11 +1,14 @@
 // Width-4 causal depthwise conv + SiLU over a packed pass (the short
 // convolution ahead of q, k, v in Gated Delta Networks' block design), never
 // reading across a prompt boundary.  Memory-bound: every input row is read
-// once per strip of 16 (bf16) or 8 (fp32) tokens, plus a 3-row halo, and
+// once per strip of 20 (bf16) or 8 (fp32) tokens, plus a 3-row halo, and
 // every output row written once.  A wave covers 256 consecutive channels of
 // one token, so each row access is a contiguous 512 B (bf16) or 1 KiB (fp32)
-// segment.  Four channels per thread keep a bf16 strip in 70 VGPRs (7 waves
-// per SIMD), which hides the load latency better than 8 channels at 3 waves.
+// segment.  Four channels per thread keep a bf16 strip in few enough VGPRs
+// for 6 or more waves per SIMD, which hides the load latency better than 8
+// channels at 3 waves.  bf16 strips stream past the caches (non-temporal
+// loads and stores) except their last three rows, which the next strip
+// reads again as its halo and so are loaded through the cache.
 #include <climits>
 
 #include "gdn_device.h"
@@ -44,29 +47,35 @@ __device__ __forceinline__ void load_ext(const ConvArgs& a, int s, int start, in
 // first is used, so a thread keeps a whole strip of loads in flight.
 template <typename IO> struct RawRow;
 template <> struct RawRow<IoBf16> {
-  static constexpr int kStrip = 16;
-  uint2 w;
-  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint2*>(p); }
+  static constexpr int kStrip = 20;
+  static constexpr bool kStream = true;   // non-temporal loads and stores
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  u2 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const u2*>(p); }
+  __device__ __forceinline__ void load_nt(const uint16_t* p) {
+    w = __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
+  }
   __device__ __forceinline__ void unpack(float* out) const {
-    out[0] = __uint_as_float(w.x << 16);
-    out[1] = __uint_as_float(w.x & 0xFFFF0000u);
-    out[2] = __uint_as_float(w.y << 16);
-    out[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    out[0] = __uint_as_float(w[0] << 16);
+    out[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+    out[2] = __uint_as_float(w[1] << 16);
+    out[3] = __uint_as_float(w[1] & 0xFFFF0000u);
   }
   // 4 values rounded to bf16 (nearest even), two per conversion
   static __device__ __forceinline__ void store(uint16_t* p, const float* v) {
     typedef float f2 __attribute__((ext_vector_type(2)));
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    uint2 o;
-    o.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[0], v[1]}, b2));
-    o.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[2], v[3]}, b2));
-    *reinterpret_cast<uint2*>(p) = o;
+    const u2 o{__builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[0], v[1]}, b2)),
+               __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[2], v[3]}, b2))};
+    __builtin_nontemporal_store(o, reinterpret_cast<u2*>(p));
   }
 };
 template <> struct RawRow<IoF32> {
   static constexpr int kStrip = 8;
+  static constexpr bool kStream = false;
   float4 a;
   __device__ __forceinline__ void load(const float* p) { a = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void load_nt(const float* p) { load(p); }
   __device__ __forceinline__ void unpack(float* out) const {
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
   }
@@ -118,8 +127,13 @@ __global__ void __launch_bounds__(kThreads) conv_silu_kernel(const ConvArgs a, i
 
   RawRow<IO> raw[kS];
 #pragma unroll
-  for (int i = 0; i < kS; ++i)
-    if (i < np) raw[i].load(xp + (size_t)(p0 + i) * a.x_stride + c0);
+  for (int i = 0; i < kS; ++i) {
+    if (i < np) {
+      const typename IO::T* row = xp + (size_t)(p0 + i) * a.x_stride + c0;
+      if (RawRow<IO>::kStream && i < kS - 3) raw[i].load_nt(row);
+      else raw[i].load(row);   // the next strip's halo: kept in the cache
+    }
+  }
 
   float w[kVec][4];
 #pragma unroll
