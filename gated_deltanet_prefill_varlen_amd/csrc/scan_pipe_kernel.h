@@ -175,12 +175,15 @@ pipelined_prefill_kernel(const ScanArgs a) {
     return __builtin_amdgcn_readfirstlane(max(max(vm4[0], vm4[1]), max(vm4[2], vm4[3])));
   };
   uint32_t vmax = 0;
-  auto rescale_if_needed = [&](uint32_t vmax) {
+  auto lane_absmax = [&]() {
     float ms = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) ms = fmaxf(ms, fabsf(S[kt][i]));
+    return ms;
+  };
+  auto rescale_if_needed = [&](uint32_t vmax, float ms) {
     const int eS = f32_exp(__uint_as_float(wave_max_u32(__float_as_uint(ms))));
     const int En = band_exp(max(eS == kNoExp ? kNoExp : eS - E, bf16_exp(vmax)));
     if (En == E) return false;
@@ -251,7 +254,16 @@ pipelined_prefill_kernel(const ScanArgs a) {
   ChunkWalk fwalk;
   fwalk.init(seq0, seq1, ci0, ckp, a.n_ckpt);
   int last_t0 = seq0, last_n = 1;
+  // the lane index as the loader uses it, formed where it is used: kept live
+  // across the loader's loop it would be spilled, and its reload waits for
+  // every row load in flight
+  auto lane_here = [&]() {
+    uint32_t l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return (int)l;
+  };
   auto fetch = [&](Rows& R) {
+    const int lane = lane_here();
     int t0x, ck_at;
     int nx = fwalk.next(CT, ckp, a.n_ckpt, t0x, ck_at);
     if (nx <= 0) { t0x = last_t0; nx = last_n; }
@@ -334,6 +346,7 @@ pipelined_prefill_kernel(const ScanArgs a) {
         sc[SC_RQ * CT + t] = t < n ? row_factor(a.l2norm, sq, aq, a.eps) : 1.0f;
       }
       if (wave == NSW) {   // betas and the base-2 cumsum of the log-gates
+        const int lane = lane_here();
         const float xg = scan32(lane < n ? R.g : 0.f) * 1.44269504088896341f;
         if (lane < CT) {
           sc[SC_G * CT + lane] = xg;
@@ -355,7 +368,7 @@ pipelined_prefill_kernel(const ScanArgs a) {
         for (int i = 0; i < 4; ++i) vm = bf16_absmax(vm, vx[i]);
       }
       vm = wave_max_u32(fold16(vm));
-      if (lane == 0) reinterpret_cast<uint32_t*>(ringSc(cs))[SC_VM * CT + wave - NSW] = vm;
+      if (lane_here() == 0) reinterpret_cast<uint32_t*>(ringSc(cs))[SC_VM * CT + wave - NSW] = vm;
     }
     // -- the rows of chunk it + 2 into R (past the last chunk the last
     //    chunk's rows again: the loads stay unconditional, so the wait for a
@@ -713,14 +726,15 @@ pipelined_prefill_kernel(const ScanArgs a) {
         const float* sCq = sc + SC_CQ * CT;
         const float* sCu = sc + SC_CU * CT;
         // X = K S0^T and QS = S0 Q^T for this wave's columns (S0 rounded to
-        // fp16 per k tile), then the chunk's decay on S.  The products are
-        // formed with the scale of the chunk before, while the chunk's own
-        // scale is chosen beside them; when it differs (rare) the held state
-        // is rescaled and the products formed again, so every chunk runs at
-        // its own scale and the update's results are not waited for before
-        // the barrier.
+        // fp16 per k tile); the chunk's decay e^{G_C} is applied to S at the
+        // update.  The products are formed with the scale of the chunk
+        // before, while the chunk's own scale is chosen beside them; when it
+        // differs (rare) the held state is rescaled and the products formed
+        // again, so every chunk runs at its own scale and the update's
+        // results are not waited for before the barrier.
         f32x16 X, QS;
         u32x2 vw[4];
+        float gC;
         {
           if (cx == 0) vmax = chunk_vmax(sc);
           auto products = [&]() {
@@ -742,26 +756,21 @@ pipelined_prefill_kernel(const ScanArgs a) {
               }
           };
           products();
+          // the lane's largest |S| for the scale choice, in the same region
+          // as the products (its maxima fill the matrix pipe's shadow)
+          const float ms = lane_absmax();
           // V of this wave's columns by transpose reads (raw bf16, before the
           // scale is known), their latency under the scale choice
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) vw[q4] = lds_tr4(sV + vtr + 8 * q4 * LDV);
           __builtin_amdgcn_sched_barrier(0);
-          if (__builtin_expect(rescale_if_needed(vmax), 0)) {   // rare: the scale changed
+          if (__builtin_expect(rescale_if_needed(vmax, ms), 0)) {   // rare: the scale changed
             __builtin_amdgcn_sched_barrier(0);
             products();
           }
           // the next chunk's largest |v|, staged two intervals ago
           if (cx + 1 < nch) vmax = chunk_vmax(ringSc(cx + 1));
-          const float gC = exp2f_hw(sc[SC_G * CT + CT - 1]);
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) S[kt][i] *= gC;
-          // the decayed state is pinned here: left free, the compiler sinks
-          // the 64 multiplies to just before the update (measured slower)
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt) asm volatile("" : "+v"(S[kt]));
+          gC = exp2f_hw(sc[SC_G * CT + CT - 1]);
         }
         // V to fp32 (scaled by 2^E), then the T and P row operands and the
         // K^T operands of the update, requested ahead
@@ -823,10 +832,15 @@ pipelined_prefill_kernel(const ScanArgs a) {
           U[4 * q4 + 2] *= c4.z; U[4 * q4 + 3] *= c4.w;
         }
         const f16x8 uh[2] = {acc_half<0>(U), acc_half<1>(U)};
+        // each tile decayed just before its first product
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) S[kt] = mma(kta[2 * kt + h2], uh[h2], S[kt]);
+          for (int i = 0; i < 16; ++i) S[kt][i] *= gC;
+          S[kt] = mma(kta[2 * kt], uh[0], S[kt]);
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) S[kt] = mma(kta[2 * kt + 1], uh[1], S[kt]);
         // the wave's 32 columns of output row t (64 bytes) go to HBM in two
         // stores: the lane pair of row t (lane halves g = 0, 1, 8-byte pieces
         // at 16 q4 + 8 g) trade pieces so that each store writes 32
