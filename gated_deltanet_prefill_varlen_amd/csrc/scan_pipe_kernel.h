@@ -776,6 +776,14 @@ pipelined_prefill_kernel(const ScanArgs a) {
         // K^T operands of the update, requested ahead
         const uint16_t* tr = bufT(cx) + c * LDT + 4 * g;
         const uint16_t* pr = ringP(cx) + c * LDT + 4 * g;
+        // beta and r_k e^G of the lane's 16 tokens, requested before the V
+        // conversion so that Y does not wait for them
+        float4 b4s[4], k4s[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          b4s[q4] = *reinterpret_cast<const float4*>(sBeta + 8 * q4 + 4 * g);
+          k4s[q4] = *reinterpret_cast<const float4*>(sCk + 8 * q4 + 4 * g);
+        }
         float vv[16];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -793,14 +801,13 @@ pipelined_prefill_kernel(const ScanArgs a) {
         // Y = beta (V - r_k e^G X), in place of X (rows past n: exact zeros)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int tb = 8 * q4 + 4 * g;
-          const float4 b4 = *reinterpret_cast<const float4*>(sBeta + tb);
-          const float4 k4 = *reinterpret_cast<const float4*>(sCk + tb);
+          const float4 b4 = b4s[q4], k4 = k4s[q4];
           const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) X[4 * q4 + r] = bb[r] * (vv[4 * q4 + r] - kk[r] * X[4 * q4 + r]);
         }
         const f16x8 pA[2] = {lds_op(pr), lds_op(pr + 16)};
+        const float cq = sCq[c];   // ahead of the K^T reads: its wait leaves them in flight
         f16x8 kta[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -813,11 +820,8 @@ pipelined_prefill_kernel(const ScanArgs a) {
         U = mma(tA[0], acc_half<0>(X), U);
         U = mma(tA[1], acc_half<1>(X), U);
         // the S0 Q^T part of the output: scale r_q e^G per token
-        {
-          const float cq = sCq[c];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) QS[i] *= cq;
-        }
+        for (int i = 0; i < 16; ++i) QS[i] *= cq;
         // O^T = scale r_q e^G (S0 Q^T) + U^T P^T, token t = c per lane: its
         // two products go ahead of the update's eight, so the output rows
         // are stored while the update is still in the matrix pipe
