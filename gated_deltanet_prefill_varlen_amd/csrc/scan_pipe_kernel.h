@@ -422,9 +422,9 @@ pipelined_prefill_kernel(const ScanArgs a) {
       *reinterpret_cast<uint32_t*>(d + (size_t)i * a.conv_dim) =
           (__float_as_uint(cr[i][0]) >> 16) | (__float_as_uint(cr[i][1]) & 0xFFFF0000u);
   };
-  // One register set of raw rows: as the conv consumes row t of a chunk,
-  // the next chunk's row t is requested into the freed register, so each
-  // row has an interval to arrive and the wave holds one chunk of rows.
+  // One register set of raw rows: once the conv has consumed a chunk's rows
+  // the next chunk's are requested into the same registers, so each row has
+  // about an interval to arrive and the wave holds one chunk of rows.
   struct RowsX {
     uint32_t x[CT];     // the lane's two channels of each row (bf16 pair)
     float g, b;         // log-gate and beta of token `lane` (wave lw 3)
@@ -475,9 +475,8 @@ pipelined_prefill_kernel(const ScanArgs a) {
         uint16_t* dst = lw == 0 ? ringQ(cs) : lw == 1 ? ringK(cs) : ringV(cs);
         uint32_t* dcol = reinterpret_cast<uint32_t*>(dst) + lane;
         const int ldw = (lw == 2 ? LDV : LDK) / 2;
-        // row t of the chunk: conv + SiLU from the carried inputs, the next
-        // chunk's row t requested into the freed register; the v wave also
-        // takes the rows' largest |v|
+        // row t of the chunk: conv + SiLU from the carried inputs; the v
+        // wave also takes the rows' largest |v|
         auto conv_row = [&](int t, bool valid, auto with_vm) {
           uint32_t o = 0;   // rows past n: zeros
           if (valid) {
@@ -489,7 +488,6 @@ pipelined_prefill_kernel(const ScanArgs a) {
             cr[2][0] = x0; cr[2][1] = x1;
             o = pack_bf16(y0, y1);
           }
-          R.x[t] = xrow(t0n, t, nn);
           dcol[t * ldw] = o;
           if constexpr (decltype(with_vm)::value) {
             vm = bf16_absmax(vm, o);
@@ -517,6 +515,11 @@ pipelined_prefill_kernel(const ScanArgs a) {
           if (cs == nch - 1 && a.conv_state_own)
             write_window(static_cast<uint16_t*>(a.conv_state_out) + (size_t)s * 3 * a.conv_dim);
         }
+        // the next chunk's rows, requested in one place (defined once per
+        // trip, the loop-carried registers need no copies, whose waits would
+        // drain these loads)
+#pragma unroll
+        for (int t = 0; t < CT; ++t) R.x[t] = xrow(t0n, t, nn);
         if (lw == 2) vm = wave_max_u32(fold16(vm));
       } else {   // betas and the base-2 cumsum of the log-gates
         const float xg = scan32(lane < n ? R.g : 0.f) * 1.44269504088896341f;
