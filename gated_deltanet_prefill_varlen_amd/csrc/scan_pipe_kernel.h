@@ -437,12 +437,21 @@ pipelined_prefill_kernel(const ScanArgs a) {
     last_t0 = t0x;
     last_n = nx;
   };
-  // row min(t, nx - 1) of the chunk at t0x, the lane's two channels (a
-  // row base held in scalar registers, the lane's offset fixed)
+  // row min(t, nx - 1) of the chunk at t0x, the lane's two channels: the
+  // chunk's base in scalar registers and a 32-bit offset per lane and row
+  // (a row's bytes times at most 31 plus the lane's channels: below 2^32
+  // for token strides under 2^23), so a row costs one vector add where a
+  // 64-bit multiply-add per lane and row was made before
+  typedef const char __attribute__((address_space(1)))* GlobalBytes;
   auto xrow = [&](int t0x, int t, int nx) {
-    const char* rp = static_cast<const char*>(a.conv_x) +
-                     (size_t)(t0x + min(t, nx - 1)) * (size_t)a.conv_x_stride * 2;
-    return *reinterpret_cast<const uint32_t*>(rp + 2 * xch);
+    const uint64_t cb = reinterpret_cast<uint64_t>(a.conv_x) + (uint64_t)t0x * (uint64_t)a.conv_x_stride * 2;
+    // (each half taken as unsigned: the builtin returns int, whose widening
+    // would copy the low half's top bit into the high half)
+    const uint32_t cb_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(cb >> 32));
+    const uint32_t cb_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)cb);
+    const GlobalBytes base = reinterpret_cast<GlobalBytes>(((uint64_t)cb_hi << 32) | (uint64_t)cb_lo);
+    const uint32_t off = (uint32_t)min(t, nx - 1) * ((uint32_t)a.conv_x_stride * 2) + 2 * (uint32_t)xch;
+    return *reinterpret_cast<const uint32_t __attribute__((address_space(1)))*>(base + off);
   };
   auto gates_x = [&](RowsX& R, int t0x, int nx) {
     const uint32_t tl = min(lane, nx - 1);
