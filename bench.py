@@ -65,9 +65,12 @@ def step_min_bytes(p, n_ckpt: int) -> int:
     """The fewest bytes one pass of the whole step can move (conv fused into
     the scan, checkpoints written once into the pool): the pre-conv rows x in
     (as many bytes as q, k, v), g and beta in, out, the final states and each
-    checkpoint once, the conv weights and each prompt's conv state."""
+    checkpoint once, the conv weights, each prompt's conv state and the conv
+    window at each checkpoint.  The same bytes are the algorithmic bytes of
+    one launch of the scan with the conv fused into its loads."""
     C = 2 * p.Hqk * p.dk + p.Hv * p.dv
-    return prefill_alg_bytes(p, n_ckpt, p.init is not None) + C * 4 * 4 + p.n_seqs * 3 * C * 2
+    return (prefill_alg_bytes(p, n_ckpt, p.init is not None) + C * 4 * 4 +
+            (p.n_seqs + n_ckpt) * 3 * C * 2)
 
 
 # The C entry points' host-side validation: no device or launch code.
@@ -220,23 +223,29 @@ def summarize_overlap(trace_dir: str) -> dict:
 
 def summarize_sq(prof_dir: str) -> dict:
     """SQ counter summaries of the prefill kernel per workload, from
-    prof_dir/sq_<workload>_p<k> (several counter passes of `--no-legs
-    --workload <workload>` runs): medians over the workload's prefill
-    dispatches, per workgroup and chunk, and busy and wait fractions.  The
-    wave-cycle counters count 4-cycle units; GRBM_GUI_ACTIVE is summed over
-    the 8 XCDs."""
+    prof_dir/sq_<run>_p<k> (several counter passes of `--no-legs --workload
+    <workload>` runs; run "chat" with `--step two-launch` for the scan alone,
+    "chatfused" for the chat wave's fused scan): medians over the workload's
+    prefill dispatches, per workgroup and chunk, and busy and wait fractions.
+    The wave-cycle counters count 4-cycle units; GRBM_GUI_ACTIVE is summed
+    over the 8 XCDs."""
     import collections
     import glob
     import workloads as W
     packs = {"chat": W.chat_wave(seed=0), "long": W.long_prompts(seed=0), "ragged": W.ragged_pack(seed=0)}
     out = {}
-    for w, p in packs.items():
+    runs = (("chat", "chat", "false"), ("conv_fused_chat", "chatfused", "true"),
+            ("long", "long", "false"), ("ragged", "ragged", "false"))
+    for key, run, variant in runs:
+        w = key.replace("conv_fused_", "")
+        p = packs[w]
         grid = {"chat": 786432, "long": 98304, "ragged": 196608}[w]
         vals = collections.defaultdict(list)
         times = []
-        for d in sorted(x for x in glob.glob(os.path.join(prof_dir, f"sq_{w}_p*")) if os.path.isdir(x)):
+        kname = f"pipelined_prefill_kernel<128, 128, {variant}>"
+        for d in sorted(x for x in glob.glob(os.path.join(prof_dir, f"sq_{run}_p*")) if os.path.isdir(x)):
             for r in _csv_rows(d, "counter_collection.csv"):
-                if "pipelined_prefill_kernel<128, 128, false>" in r["Kernel_Name"] and int(r["Grid_Size"]) == grid:
+                if kname in r["Kernel_Name"] and int(r["Grid_Size"]) == grid:
                     vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
                     if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
                         times.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -252,7 +261,7 @@ def summarize_sq(prof_dir: str) -> dict:
         t_us = statistics.median(times)
         per = {k: m[k] / chunks for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
                                           "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR") if k in m}
-        out[w] = {
+        out[key] = {
             "workgroups": wgs, "chunks": chunks, "dispatches": len(times), "dispatch_us": t_us,
             "clock_GHz": cycles / t_us / 1e3,
             "per_workgroup_chunk": per,
@@ -923,6 +932,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-prompts", type=int, default=32)
     ap.add_argument("--workload", default="chat", choices=["chat", "long", "ragged"])
+    ap.add_argument("--step", default="fused", choices=["fused", "two-launch"],
+                    help="chat wave: the conv fused into the scan's loads (one launch; the faster here) "
+                         "or the conv kernel then the scan; the other one is timed as a leg")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="summarize a rocprofv3 run set of this script (no GPU) and exit")
     ap.add_argument("--overlap-only", action="store_true",
@@ -963,14 +975,22 @@ def main():
     p = fn(seed=0, with_conv=True) if args.workload == "chat" else fn(seed=0)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
+    fused = args.workload == "chat" and args.step == "fused"
+    step_labels = {True: ": conv1d+SiLU fused into the scan's loads (one launch, checkpoints), checkpoint "
+                         "copy on its own stream",
+                   False: ": conv1d+SiLU, scan with checkpoints, checkpoint copy on its own stream"}
     if args.workload == "chat":
-        log("[bench] timing headline step (conv, scan, checkpoint copy)")
-        label += ": conv1d+SiLU, scan with checkpoints, checkpoint copy on its own stream"
-        step = bench_layer_step(torch, gdn, p, args.steps, args.warmup, stream, label)
+        log(f"[bench] timing headline step ({'conv fused into the scan' if fused else 'conv, scan'}, "
+            "checkpoint copy)")
+        label += step_labels[fused]
+        step = bench_layer_step(torch, gdn, p, args.steps, args.warmup, stream, label, fused=fused)
+        # the dominant launch: the fused scan moves the step's fewest bytes (x
+        # in place of q, k, v, plus the conv weights, states and windows)
         head = {"workload": label, "ms_median": step["ms_per_step"], "tokens_per_s": step["tokens_per_s"],
                 "ms_p10": step["step_spacing_ms_p10"], "ms_p90": step["step_spacing_ms_p90"],
                 "checkpoints": step["checkpoints"],
-                "alg_bytes": step["scan_alg_bytes"], "alg_flops": step["scan_alg_flops"],
+                "alg_bytes": step["step_min_bytes"] if fused else step["scan_alg_bytes"],
+                "alg_flops": step["scan_alg_flops"],
                 "scan_ms_mean": step["scan_ms_mean"], "step": step}
     else:
         log("[bench] timing headline step (scan)")
@@ -992,13 +1012,19 @@ def main():
             log(f"[bench] leg {name}")
             legs[name] = f(torch, gdn, stream, flush, 10)
         if args.workload == "chat":
-            log("[bench] leg step_conv_fused")
-            legs["step_conv_fused"] = bench_layer_step(
-                torch, gdn, p, args.steps, args.warmup, stream,
-                makers["chat"][1] + ": the conv fused into the scan's loads (one launch), checkpoint copy "
-                "on its own stream", fused=True)
-            legs["step_conv_fused"]["vs_two_launches"] = (legs["step_conv_fused"]["ms_per_step"] /
-                                                          head["ms_median"])
+            other = "step_two_launches" if fused else "step_conv_fused"
+            log(f"[bench] leg {other}")
+            o = bench_layer_step(torch, gdn, p, args.steps, args.warmup, stream,
+                                 makers["chat"][1] + step_labels[not fused], fused=not fused)
+            o["vs_headline_step"] = o["ms_per_step"] / head["ms_median"]
+            # the unfused scan's own roofline inside its step
+            sb = o["scan_alg_bytes"] if fused else step["scan_alg_bytes"]
+            sm = o["scan_ms_mean"] if fused else step["scan_ms_mean"]
+            o["scan_roofline"] = {"kernel": "pipelined_prefill_kernel<128,128,false>", "alg_bytes_per_launch": sb,
+                                  "launch_ms_mean": sm, "achieved_GBs": sb / (sm * 1e-3) / 1e9,
+                                  "frac": sb / (sm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                  "traffic": measured_traffic("chat")}
+            legs[other] = o
             log("[bench] leg conv_fused_packs")
             legs["conv_fused_packs"] = bench_conv_fused_packs(torch, gdn, stream, flush, 10, W)
             log("[bench] leg scan_only")
@@ -1038,8 +1064,8 @@ def main():
                    "checkpoint_block": p.block, "checkpoints": head["checkpoints"],
                    "timing": ("K steps queued back to back between two device synchronisations, "
                               "each step's checkpoint copy on its own stream right after its scan, "
-                              "beside the next step's conv, the last copy joined; ms_per_step = "
-                              "HIP-event time of the "
+                              "beside the next step's " + ("fused scan" if fused else "conv") +
+                              ", the last copy joined; ms_per_step = HIP-event time of the "
                               "region / K" if args.workload == "chat" else
                               "median of per-launch HIP-event times on the launch stream; 1 GiB "
                               "cache flush before each launch, outside the events"),
@@ -1049,8 +1075,10 @@ def main():
         "step": head.get("step"),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(args.workload),
-                     "kernel": "pipelined_prefill_kernel<128,128>", "alg_bytes_per_launch": head["alg_bytes"],
+                     "traffic": measured_traffic(("conv_fused_" if fused else "") + args.workload),
+                     "kernel": ("pipelined_prefill_kernel<128,128,true> (the conv in its loads)" if fused
+                                else "pipelined_prefill_kernel<128,128,false>"),
+                     "alg_bytes_per_launch": head["alg_bytes"],
                      "launch_ms_mean": head["scan_ms_mean"],
                      "mfma_alg_tflops": head["alg_flops"] / mean_s / 1e12},
         "step_roofline": ({"bound": "hbm", "alg_bytes_min": head["step"]["step_min_bytes"],
@@ -1060,7 +1088,7 @@ def main():
                            / HBM_PEAK_GBS,
                            "note": "whole step (conv, scan, checkpoint copy) against the fewest bytes "
                                    "one pass can move: x, g, beta in, out, final states and "
-                                   "checkpoints once, conv weights and states"}
+                                   "checkpoints once, conv weights, states and windows"}
                           if head.get("step") else None),
         "cpu_baseline": cpu,
         "legs": legs,

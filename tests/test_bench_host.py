@@ -49,10 +49,13 @@ def test_algorithmic_flops_at_the_executed_chunk():
     assert B.prefill_alg_flops(p) == pytest.approx(32768 * 32 * per)
 
 
-def test_step_min_bytes_adds_only_the_conv_weights_and_states():
+def test_step_min_bytes_adds_only_the_conv_weights_states_and_windows():
     p = chat_shape()
     conv_dim = 2 * 16 * 128 + 32 * 128
-    assert B.step_min_bytes(p, 96) == B.prefill_alg_bytes(p, 96, False) + conv_dim * 16 + 32 * 3 * conv_dim * 2
+    # fp32 weights [conv_dim, 4]; bf16 conv states [32, 3, conv_dim] and windows [96, 3, conv_dim]
+    assert B.step_min_bytes(p, 96) == (B.prefill_alg_bytes(p, 96, False) + conv_dim * 16 +
+                                       (32 + 96) * 3 * conv_dim * 2)
+    assert B.step_min_bytes(p, 96) == 1082130432 + 131072 + 6291456
 
 
 def _write_csv(path, rows):
