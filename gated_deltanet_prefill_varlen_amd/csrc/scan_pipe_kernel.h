@@ -377,58 +377,82 @@ pipelined_prefill_kernel(const ScanArgs a) {
   };
 
   // ---- the short conv in the loads (CONV): the loader waves read the
-  //      pre-conv rows x and apply the width-4 causal conv and SiLU.  Loader
-  //      wave lw owns two channels per lane of one tensor for all rows of a
-  //      chunk (lw 0: q of qk head j, 1: k, 2: v of head h), so a channel's
-  //      three earlier inputs are the lane's own earlier rows: carried from
-  //      chunk to chunk, and from the prompt's conv state before its first
-  //      token.  Wave lw 3 loads the gates.  The conv output, rounded to
-  //      bf16 in conv1d_silu's operation order, is written to the ring slot
-  //      as bf16; the Gram and K Q^T waves convert the k and q tiles to fp16
-  //      in place (convert_tile), with the sums and scalings of the unfused
-  //      staging, so the scan sees the values, norms and scales the separate
-  //      conv and scan give.
+  //      pre-conv rows x and apply the width-4 causal conv and SiLU.  The
+  //      four loader waves split a chunk's rows: wave lw convolves rows
+  //      8 lw .. 8 lw + 7 of the three tensors, two channels per lane of
+  //      each (q and k of qk head j, v of head h), from those rows and the
+  //      three before them, all requested one interval ahead; before the
+  //      prompt's first token the three inputs come from its conv state (or
+  //      are zeros).  Wave lw 3 also loads the gates.  The conv output,
+  //      rounded to bf16 in conv1d_silu's operation order, is written to the
+  //      ring slot as bf16; the Gram and K Q^T waves convert the k and q
+  //      tiles to fp16 in place (convert_tile), with the sums and scalings of
+  //      the unfused staging, so the scan sees the values, norms and scales
+  //      the separate conv and scan give.
   const int lw = wave - NSW;
-  float cw[2][4], cr[3][2];   // the lane's conv weights and last three inputs
-  int xch = 0;                // the lane's first channel
-  bool own_win = false;       // this workgroup writes the lane's conv windows
+  constexpr int XR = CT / C::NLW;   // rows per loader wave
+  constexpr int XH = XR + 3;        // with the three before them
+  uint32_t xoff[3] = {0u, 0u, 0u};  // the lane's channel pair in q, k, v (element index in a row)
+  float cw[3][2][4];                // its conv weights (taps as the conv kernel scales them)
+  // the q/k windows are written by the first value head of each qk head
+  const bool own_qk = h % (a.Hv / a.Hqk) == 0;
   if constexpr (CONV) {
-    if (wave >= NSW && wave < NSW + C::NLW && lw < 3) {
-      xch = (lw == 0 ? j * DK : lw == 1 ? (a.Hqk + j) * DK : 2 * a.Hqk * DK + h * DV) + 2 * lane;
-      // q/k windows once per qk head (by its first value head), v by every head
-      own_win = lw == 2 || h % (a.Hv / a.Hqk) == 0;
+    if (wave >= NSW && wave < NSW + C::NLW) {
+      xoff[0] = (uint32_t)(j * DK + 2 * lane);
+      xoff[1] = (uint32_t)((a.Hqk + j) * DK + 2 * lane);
+      xoff[2] = (uint32_t)(2 * a.Hqk * DK + h * DV + 2 * lane);
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const float4 w4 = reinterpret_cast<const float4*>(a.conv_w)[xch + c2];
-        cw[c2][0] = conv_tap(w4.x); cw[c2][1] = conv_tap(w4.y);
-        cw[c2][2] = conv_tap(w4.z); cw[c2][3] = conv_tap(w4.w);
-      }
+      for (int tn = 0; tn < 3; ++tn)
 #pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        uint32_t w = 0;
-        if (a.conv_state_in)
-          w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.conv_state_in) +
-                                                 ((size_t)s * 3 + i) * a.conv_dim + xch);
-        cr[i][0] = __uint_as_float(w << 16);
-        cr[i][1] = __uint_as_float(w & 0xFFFF0000u);
-      }
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const float4 w4 = reinterpret_cast<const float4*>(a.conv_w)[xoff[tn] + c2];
+          cw[tn][c2][0] = conv_tap(w4.x); cw[tn][c2][1] = conv_tap(w4.y);
+          cw[tn][c2][2] = conv_tap(w4.z); cw[tn][c2][3] = conv_tap(w4.w);
+        }
     }
   }
-  // the lane's three carried inputs (exact bf16 values) as a conv window
-  auto write_window = [&](void* dst3) {
-    uint16_t* d = static_cast<uint16_t*>(dst3) + xch;
+  // the lane's channel pair of tensor tn at token position p of this
+  // prompt or, before its first token, from its conv state (zeros without
+  // one), as a bf16 pair
+  auto x_input = [&](int p, int tn) -> uint32_t {
+    // (the offset passed through an empty asm: these rare reads' addresses
+    // are then formed here, not hoisted out of the loader's loop into
+    // registers it has none to spare for)
+    uint32_t xo = xoff[tn];
+    asm volatile("" : "+v"(xo));
+    if (p >= seq0)
+      return *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.conv_x) +
+                                                (size_t)p * a.conv_x_stride + xo);
+    if (!a.conv_state_in) return 0u;
+    return *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.conv_state_in) +
+                                              ((size_t)s * 3 + (p - seq0 + 3)) * a.conv_dim + xo);
+  };
+  // the three inputs before position e as a conv window at dst3 ([3,
+  // conv_dim]); all reads come before the writes (dst3 may be the state read)
+  auto write_window = [&](void* dst3, int e) {
+    uint32_t w[3][3];
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
-      *reinterpret_cast<uint32_t*>(d + (size_t)i * a.conv_dim) =
-          (__float_as_uint(cr[i][0]) >> 16) | (__float_as_uint(cr[i][1]) & 0xFFFF0000u);
+    for (int tn = 0; tn < 3; ++tn)
+#pragma unroll
+      for (int i = 0; i < 3; ++i) w[tn][i] = x_input(e - 3 + i, tn);
+    uint16_t* d = static_cast<uint16_t*>(dst3);
+#pragma unroll
+    for (int tn = 0; tn < 3; ++tn)
+      if (tn == 2 || own_qk) {
+        uint32_t xo = xoff[tn];
+        asm volatile("" : "+v"(xo));
+#pragma unroll
+        for (int i = 0; i < 3; ++i) *reinterpret_cast<uint32_t*>(d + (size_t)i * a.conv_dim + xo) = w[tn][i];
+      }
   };
   // One register set of raw rows: once the conv has consumed a chunk's rows
   // the next chunk's are requested into the same registers, so each row has
-  // about an interval to arrive and the wave holds one chunk of rows.
+  // about an interval to arrive.
   struct RowsX {
-    uint32_t x[CT];     // the lane's two channels of each row (bf16 pair)
+    uint32_t x[XH][3];  // rows 8 lw - 3 .. 8 lw + 7 of the chunk: the lane's pair of q, k, v
     float g, b;         // log-gate and beta of token `lane` (wave lw 3)
-    int n, ck;          // the chunk's tokens; the checkpoint it ends at (or -1)
+    int n, ck, t0;      // the chunk's tokens, the checkpoint it ends at (or -1), its first token
+    int zero;           // rows r < 3 to take as zeros (before the prompt, no conv state)
   };
   // the walk's next chunk (past the last one: the last again, no checkpoint)
   auto next_x = [&](int& t0x, int& nx, int& ck_at) {
@@ -437,21 +461,45 @@ pipelined_prefill_kernel(const ScanArgs a) {
     last_t0 = t0x;
     last_n = nx;
   };
-  // row min(t, nx - 1) of the chunk at t0x, the lane's two channels: the
-  // chunk's base in scalar registers and a 32-bit offset per lane and row
-  // (a row's bytes times at most 31 plus the lane's channels: below 2^32
-  // for token strides under 2^23), so a row costs one vector add where a
-  // 64-bit multiply-add per lane and row was made before
+  // The wave's rows of the chunk at t0x: row t = 8 lw - 3 + r (clamped to
+  // the chunk's last row), each load from a wave-uniform base in scalar
+  // registers and a 32-bit offset per lane (a row's bytes times at most 34
+  // plus the lane's channels: below 2^32 for token strides under 2^23), with
+  // no branch: a row before the prompt's first token (wave 0 only) reads the
+  // prompt's conv state, or, without one, a row that is then taken as zeros.
   typedef const char __attribute__((address_space(1)))* GlobalBytes;
-  auto xrow = [&](int t0x, int t, int nx) {
-    const uint64_t cb = reinterpret_cast<uint64_t>(a.conv_x) + (uint64_t)t0x * (uint64_t)a.conv_x_stride * 2;
+  auto uniform_base = [&](uint64_t p) {
     // (each half taken as unsigned: the builtin returns int, whose widening
     // would copy the low half's top bit into the high half)
-    const uint32_t cb_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(cb >> 32));
-    const uint32_t cb_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)cb);
-    const GlobalBytes base = reinterpret_cast<GlobalBytes>(((uint64_t)cb_hi << 32) | (uint64_t)cb_lo);
-    const uint32_t off = (uint32_t)min(t, nx - 1) * ((uint32_t)a.conv_x_stride * 2) + 2 * (uint32_t)xch;
-    return *reinterpret_cast<const uint32_t __attribute__((address_space(1)))*>(base + off);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+    return reinterpret_cast<GlobalBytes>(((uint64_t)hi << 32) | (uint64_t)lo);
+  };
+  auto fetch_x = [&](RowsX& R, int t0x, int nx) {
+    const uint32_t rb = (uint32_t)a.conv_x_stride * 2;
+    const uint64_t xb = reinterpret_cast<uint64_t>(a.conv_x) + ((uint64_t)t0x - 3) * (uint64_t)rb;
+    int zero = 0;
+#pragma unroll
+    for (int r = 0; r < XH; ++r) {
+      const int t = XR * lw - 3 + r;
+      uint64_t base = xb;
+      uint32_t roff = (uint32_t)(min(t, nx - 1) + 3) * rb;
+      if (r < 3) {
+        const bool hist = lw == 0 && t0x + t < seq0;   // before the prompt's first token
+        const uint64_t hb = a.conv_state_in
+            ? reinterpret_cast<uint64_t>(a.conv_state_in) + ((uint64_t)s * 3 + (t0x + t - seq0 + 3)) * a.conv_dim * 2
+            : reinterpret_cast<uint64_t>(a.conv_x);
+        base = hist ? hb : xb;
+        roff = hist ? 0u : roff;
+        zero |= (hist && !a.conv_state_in) ? 1 << r : 0;
+      }
+      const GlobalBytes bp = uniform_base(base);
+#pragma unroll
+      for (int tn = 0; tn < 3; ++tn)
+        R.x[r][tn] = *reinterpret_cast<const uint32_t __attribute__((address_space(1)))*>(bp + (roff + 2 * xoff[tn]));
+    }
+    R.zero = zero;
+    R.t0 = t0x;
   };
   auto gates_x = [&](RowsX& R, int t0x, int nx) {
     const uint32_t tl = min(lane, nx - 1);
@@ -463,12 +511,8 @@ pipelined_prefill_kernel(const ScanArgs a) {
     next_x(t0x, nx, ck_at);
     R.n = nx;
     R.ck = ck_at;
-    if (lw < 3) {
-#pragma unroll
-      for (int t = 0; t < CT; ++t) R.x[t] = xrow(t0x, t, nx);
-    } else {
-      gates_x(R, t0x, nx);
-    }
+    fetch_x(R, t0x, nx);
+    if (lw == 3) gates_x(R, t0x, nx);
   };
   // the loader waves' part of interval it with the conv: chunk it staged
   // from R, which takes the rows of chunk it + 1
@@ -479,58 +523,63 @@ pipelined_prefill_kernel(const ScanArgs a) {
     if (cs < nch) {
       const int n = R.n;
       float* sc = ringSc(cs);
-      uint32_t vm = 0;
-      if (lw < 3) {
-        uint16_t* dst = lw == 0 ? ringQ(cs) : lw == 1 ? ringK(cs) : ringV(cs);
-        uint32_t* dcol = reinterpret_cast<uint32_t*>(dst) + lane;
-        const int ldw = (lw == 2 ? LDV : LDK) / 2;
-        // row t of the chunk: conv + SiLU from the carried inputs; the v
-        // wave also takes the rows' largest |v|
-        auto conv_row = [&](int t, bool valid, auto with_vm) {
-          uint32_t o = 0;   // rows past n: zeros
+      uint32_t* dcol[3] = {reinterpret_cast<uint32_t*>(ringQ(cs)) + lane, reinterpret_cast<uint32_t*>(ringK(cs)) + lane,
+                           reinterpret_cast<uint32_t*>(ringV(cs)) + lane};
+      constexpr int ldw[3] = {LDK / 2, LDK / 2, LDV / 2};
+      uint32_t vm = 0;   // the largest |v| of the wave's rows (bf16 bits)
+      if (R.zero) {   // rows before the prompt with no conv state: zeros (rare)
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+          if (R.zero & (1 << r))
+#pragma unroll
+            for (int tn = 0; tn < 3; ++tn) R.x[r][tn] = 0u;
+      }
+      // row 8 lw + r of the chunk: conv + SiLU of its three tensors from
+      // the wave's rows r .. r + 3 (zeros past n)
+      auto conv_row = [&](int r, bool valid) {
+        const int t = XR * lw + r;
+#pragma unroll
+        for (int tn = 0; tn < 3; ++tn) {
+          uint32_t o = 0;
           if (valid) {
-            const float x0 = __uint_as_float(R.x[t] << 16), x1 = __uint_as_float(R.x[t] & 0xFFFF0000u);
-            const float y0 = conv4_silu(cw[0][0], cw[0][1], cw[0][2], cw[0][3], cr[0][0], cr[1][0], cr[2][0], x0);
-            const float y1 = conv4_silu(cw[1][0], cw[1][1], cw[1][2], cw[1][3], cr[0][1], cr[1][1], cr[2][1], x1);
-            cr[0][0] = cr[1][0]; cr[0][1] = cr[1][1];
-            cr[1][0] = cr[2][0]; cr[1][1] = cr[2][1];
-            cr[2][0] = x0; cr[2][1] = x1;
-            o = pack_bf16(y0, y1);
-          }
-          dcol[t * ldw] = o;
-          if constexpr (decltype(with_vm)::value) {
-            vm = bf16_absmax(vm, o);
-            asm volatile("" : "+v"(vm));   // taken here: deferred, it keeps every row's output live
-          }
-        };
-        auto conv_rows = [&](auto with_vm) {
-          if (n == CT) {   // a whole chunk: no branches, the rows interleave
+            float y[2];
 #pragma unroll
-            for (int t = 0; t < CT; ++t) {
-              conv_row(t, true, with_vm);
-              if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // four rows in flight
+            for (int c2 = 0; c2 < 2; ++c2) {
+              auto in = [&](int q) {
+                const uint32_t u = R.x[r + q][tn];
+                return c2 == 0 ? __uint_as_float(u << 16) : __uint_as_float(u & 0xFFFF0000u);
+              };
+              y[c2] = conv4_silu(cw[tn][c2][0], cw[tn][c2][1], cw[tn][c2][2], cw[tn][c2][3], in(0), in(1), in(2),
+                                 in(3));
             }
-          } else {
-#pragma unroll
-            for (int t = 0; t < CT; ++t) conv_row(t, t < n, with_vm);
+            o = pack_bf16(y[0], y[1]);
           }
-        };
-        if (lw == 2)
-          conv_rows(std::true_type{});
-        else
-          conv_rows(std::false_type{});
-        if (own_win) {
-          if (R.ck >= 0 && a.conv_ckpt) write_window(static_cast<uint16_t*>(a.conv_ckpt) + (size_t)R.ck * 3 * a.conv_dim);
-          if (cs == nch - 1 && a.conv_state_own)
-            write_window(static_cast<uint16_t*>(a.conv_state_out) + (size_t)s * 3 * a.conv_dim);
+          dcol[tn][t * ldw[tn]] = o;
+          if (tn == 2) vm = bf16_absmax(vm, o);
         }
-        // the next chunk's rows, requested in one place (defined once per
-        // trip, the loop-carried registers need no copies, whose waits would
-        // drain these loads)
+      };
+      if (XR * lw + XR <= n) {   // all the wave's rows in the chunk: no branches
 #pragma unroll
-        for (int t = 0; t < CT; ++t) R.x[t] = xrow(t0n, t, nn);
-        if (lw == 2) vm = wave_max_u32(fold16(vm));
-      } else {   // betas and the base-2 cumsum of the log-gates
+        for (int r = 0; r < XR; ++r) {
+          conv_row(r, true);
+          __builtin_amdgcn_sched_barrier(0);   // one row at a time: wider, the loop spills
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < XR; ++r) conv_row(r, XR * lw + r < n);
+      }
+      if (lw == 0) {   // conv windows: at a checkpoint, and the prompt's conv state
+        if (R.ck >= 0 && a.conv_ckpt)
+          write_window(static_cast<uint16_t*>(a.conv_ckpt) + (size_t)R.ck * 3 * a.conv_dim, R.t0 + n);
+        if (cs == nch - 1 && a.conv_state_own)
+          write_window(static_cast<uint16_t*>(a.conv_state_out) + (size_t)s * 3 * a.conv_dim, R.t0 + n);
+      }
+      // the next chunk's rows, requested in one place (defined once per
+      // trip, the loop-carried registers need no copies, whose waits would
+      // drain these loads)
+      fetch_x(R, t0n, nn);
+      vm = wave_max_u32(fold16(vm));
+      if (lw == 3) {   // betas and the base-2 cumsum of the log-gates
         const float xg = scan32(lane < n ? R.g : 0.f) * 1.44269504088896341f;
         if (lane < CT) {
           sc[SC_G * CT + lane] = xg;
@@ -539,8 +588,8 @@ pipelined_prefill_kernel(const ScanArgs a) {
         if (lane == 0) reinterpret_cast<int*>(sc)[SC_VM * CT + 4] = n;   // for the factor waves
         gates_x(R, t0n, nn);
       }
-      // the chunk's largest |v| (bf16 bits): the v wave's, zeros beside it
-      if (lane == 0) reinterpret_cast<uint32_t*>(sc)[SC_VM * CT + lw] = lw == 2 ? vm : 0u;
+      // the chunk's largest |v| (bf16 bits): one partial per loader wave
+      if (lane == 0) reinterpret_cast<uint32_t*>(sc)[SC_VM * CT + lw] = vm;
     }
     R.n = nn;
     R.ck = ckn;
@@ -918,8 +967,8 @@ pipelined_prefill_kernel(const ScanArgs a) {
   } else {
     // an empty prompt: its conv state passes through
     if constexpr (CONV)
-      if (lw < 3 && own_win && a.conv_state_own)
-        write_window(static_cast<uint16_t*>(a.conv_state_out) + (size_t)s * 3 * a.conv_dim);
+      if (lw == 0 && a.conv_state_own)
+        write_window(static_cast<uint16_t*>(a.conv_state_out) + (size_t)s * 3 * a.conv_dim, seq0);
     for (int it = 0; it < nint; ++it) __syncthreads();
   }
   if (wave < NSW && a.final_state)
