@@ -600,7 +600,7 @@ pipelined_prefill_kernel(const ScanArgs a) {
   // of row r), pieces, sums and scalings, so the values and the row factors
   // rf[t] are the unfused kernel's.
   auto convert_tile = [&](uint16_t* sT, float* rf, int n) {
-#pragma unroll 1
+#pragma unroll 2   // two passes at a time (four: the factor loop spills)
     for (int p8 = 0; p8 < CT / 8; ++p8) {
       const int t = 8 * p8 + lane / 8, pc = lane % 8;
       u32x4 x[2];   // 8-byte reads: rows are 8-byte aligned
