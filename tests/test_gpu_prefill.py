@@ -115,7 +115,7 @@ def test_pipelined_empty_prompts_and_strided_views():
     assert_parity(dp, all_pairs(p))
 
 
-@pytest.mark.parametrize("hqk,hv", [(4, 4), (1, 4), (2, 8)])
+@pytest.mark.parametrize("hqk,hv", [(4, 4), (1, 4), (2, 8), (2, 6)])
 def test_pipelined_gqa_ratios(hqk, hv):
     p = W.make_pack("gqa", [150, 1, 95, 64], hqk, hv, 128, 128, 64, 64, seed=10 * hqk + hv, init_std=0.1)
     dp = DevPack(p, _ckpt(p)).run()

@@ -11,9 +11,10 @@ followed by its recurrence on sampled (prompt, head) pairs.
 
 Cases: prompts of 0 to 3 tokens (windows reaching into the conv state),
 lengths on both sides of the 32-token tile, checkpoints on and off the tile
-grid (also at a prompt's first and second token), GQA groups of 2 and 1,
-conv states in or NULL, written in place or to their own buffer, no windows
-or states asked for, a padded x row stride, inputs far from unit scale
+grid (also at a prompt's first and second token), GQA groups of 1 to 4 (all
+with the XCD-paired grid order), conv states in or NULL, written in place or
+to their own buffer, no windows or states asked for, a padded x row stride,
+inputs far from unit scale
 (q/k rows scaled into fp16 range), the full chat wave and long prompts."""
 import numpy as np
 import pytest
@@ -126,7 +127,7 @@ def mixed_ckpts(p):
     return np.array(sorted(ck), np.int32)
 
 
-@pytest.mark.parametrize("Hqk,Hv", [(2, 4), (2, 2)])
+@pytest.mark.parametrize("Hqk,Hv", [(2, 4), (2, 2), (2, 8), (2, 6)])
 def test_fused_equals_two_launches_ragged(Hqk, Hv):
     p = small_pack(LENGTHS, Hqk, Hv)
     ck = mixed_ckpts(p)
