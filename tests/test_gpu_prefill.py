@@ -177,11 +177,11 @@ def _full_size(p, pairs):
 
 
 @pytest.mark.slow
-def test_chat_wave_full_size_sampled():
-    """64 of the 1,024 (prompt, head) pairs, every output row and checkpoint
-    of each, in the launch configuration the benchmark times."""
+def test_chat_wave_full_size_all_pairs():
+    """All 1,024 (prompt, head) pairs, every output row and checkpoint of
+    each, in the launch configuration the benchmark times."""
     p = W.chat_wave()
-    ck, (eo, es) = _full_size(p, sample_pairs(p, 64))
+    ck, (eo, es) = _full_size(p, all_pairs(p))
     assert len(ck) == 96
     print(f"chat wave: out {eo:.2e} state {es:.2e}")
 

@@ -182,7 +182,7 @@ def test_fused_chat_wave_bitwise_and_sampled_oracle():
     got = c.fused()
     torch.cuda.synchronize()
     assert_same(ref, got, "chat wave")
-    pairs = sample_pairs(p, 16, seed=11)
+    pairs = sample_pairs(p, 64, seed=11)
     refs = oracle_pairs(p, pairs, ck, conv=True)
     wo, ws = compare_pairs(p, pairs, refs, to_f64(got["out"]), to_f64(got["final"]), to_f64(got["ckbuf"]), ck)
     print(f"chat wave fused vs oracle: out {wo:.2e} state {ws:.2e}")
