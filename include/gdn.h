@@ -209,6 +209,12 @@ GDN_API gdn_status gdn_prefill_packed(const gdn_shape* shape, const int32_t* cu_
  * views q = y[:, :Hqk*dk], k = y[:, Hqk*dk:2*Hqk*dk], v = y[:, 2*Hqk*dk:],
  * bit for bit: the conv runs in conv1d_silu's operation order and its bf16
  * outputs are converted for the products exactly as loaded ones are.
+ * Performance: the conv's arithmetic runs on the workgroups of the scan, one
+ * per (prompt, value head).  On MI355X this is the faster path when those
+ * fill the 256 CUs several times over (32 x 1,024 tokens, 32 value heads:
+ * 13% below the two launches); with fewer (prompt, head) pairs than CUs
+ * (4 prompts x 32 heads) the two launches are faster, since the separate
+ * conv uses the whole chip.
  *   shape:           bf16 io, dk = dv = 128, chunk 32 or 64 (the scan's
  *                    32-token tiles); other shapes: GDN_ERR_UNSUPPORTED.
  *                    q/k/v_tok_stride are not used.
